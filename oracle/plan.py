@@ -1,0 +1,162 @@
+"""Reference work partition (plan) for the persistent attention kernels (test infrastructure only).
+
+The FlashInfer paper summary [FI-paper, research methodology 3: dynamic
+load-balanced scheduling] says only that compile-time tile sizes are
+decoupled from runtime scheduling, that a CPU plan built from the
+requests' runtime lengths spreads the work evenly over all cores, and that
+the plan is cached on the GPU so one fixed, graph-compatible launch
+executes it; [FI-PR5329, code analysis 1] adds that the persistent kernel
+runs two tile classes (128- and 16-row query tiles) on a grid fixed by the
+plan.  The pages give no algorithm, so this module *defines* one, in
+integer arithmetic with every tie broken explicitly, so that an
+independent implementation can match it bit for bit:
+
+1. Units.  For each request r with qo_len > 0 and kv_len > 0, each kv head
+   h, and each query tile t: the request's rows are (token i, group member
+   u) flattened as row = i*g + u; tile t covers rows
+   [t*tile_q, min((t+1)*tile_q, qo_len*g)).  With i_lo / i_hi the first /
+   last token of the tile and qpos(i) = kv_len - qo_len + i, the tile needs
+   keys [lo, hi) with hi = min(kv_len, qpos(i_hi)+1) if causal else kv_len,
+   lo = max(0, qpos(i_lo) - window + 1) if window > 0 else 0, plus the sink
+   range [0, min(sink, lo)) when window > 0 and lo > 0.
+2. Total cost C = sum over units of (hi - lo) + |sink range|.
+3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W*split_factor)), tile_kv)),
+   then min(L_c, max_chunk) when max_chunk > 0.
+4. Chunks of a unit: for k = lo // L_c .. (hi-1) // L_c the range
+   [max(lo, k*L_c), min(hi, (k+1)*L_c)) (boundaries at absolute multiples of
+   L_c), then the non-empty sink range as the unit's last chunk.
+5. Items are created in unit order (r, h, t ascending), then chunk order;
+   item id = creation index; cost = length + item_overhead.  A unit with
+   >= 2 chunks gives its items consecutive partial-state slots from a
+   global counter; a single-chunk unit's item has slot -1 (writes the
+   output directly).
+6. Assignment (longest processing time first): items ordered by (cost
+   descending, id ascending); a min-heap of (load, worker) starting at
+   (0, w); each item pops the minimum (lexicographic), joins that worker's
+   list, and (load + cost, worker) is pushed back.
+7. Merge table: one entry per unit with >= 2 chunks, in unit order:
+   (r, h, row_lo, row_hi, first_slot, n_chunks).
+8. Capacities: more than max_items_per_worker items on a worker, more than
+   max_slots slots or more than max_merge merge entries is an error.
+
+Pinned by: the partition covers every (unit, visible key) exactly once,
+chunk starts fall on multiples of L_c, the LPT makespan bound, greedy
+optimality of each step, and a committed golden plan (tests).
+"""
+from __future__ import annotations
+
+import dataclasses
+import heapq
+
+import numpy as np
+
+
+class PlanError(Exception):
+    def __init__(self, code: str, msg: str):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+@dataclasses.dataclass
+class PlanParams:
+    num_qo_heads: int
+    num_kv_heads: int
+    tile_q: int
+    tile_kv: int
+    num_workers: int
+    split_factor: int
+    min_chunk: int
+    max_chunk: int
+    item_overhead: int
+    max_items_per_worker: int
+    max_slots: int
+    max_merge: int
+    causal: bool = False
+    window: int = 0
+    sink: int = 0
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
+    qo_len = [int(x) for x in qo_len]
+    kv_len = [int(x) for x in kv_len]
+    if p.num_kv_heads <= 0 or p.num_qo_heads % p.num_kv_heads:
+        raise PlanError("INVALID_ARG", "num_qo_heads must be a positive multiple of num_kv_heads")
+    g = p.num_qo_heads // p.num_kv_heads
+    for Q, L in zip(qo_len, kv_len):
+        if Q < 0 or L < 0 or Q > L:
+            raise PlanError("INVALID_ARG", "need 0 <= qo_len <= kv_len")
+    W = p.num_workers
+
+    units = []  # (r, h, row_lo, row_hi, lo, hi, sink_hi)
+    for r, (Q, L) in enumerate(zip(qo_len, kv_len)):
+        if Q == 0 or L == 0:
+            continue
+        rows = Q * g
+        for h in range(p.num_kv_heads):
+            for t in range(_ceil_div(rows, p.tile_q)):
+                row_lo = t * p.tile_q
+                row_hi = min(rows, (t + 1) * p.tile_q)
+                i_lo, i_hi = row_lo // g, (row_hi - 1) // g
+                qpos_lo, qpos_hi = L - Q + i_lo, L - Q + i_hi
+                hi = min(L, qpos_hi + 1) if p.causal else L
+                lo = max(0, qpos_lo - p.window + 1) if p.window > 0 else 0
+                sink_hi = min(p.sink, lo) if (p.window > 0 and lo > 0) else 0
+                units.append((r, h, row_lo, row_hi, lo, hi, sink_hi))
+
+    C = sum((hi - lo) + sink_hi for (_, _, _, _, lo, hi, sink_hi) in units)
+    Lc = max(p.min_chunk, _ceil_div(_ceil_div(C, W * p.split_factor), p.tile_kv) * p.tile_kv)
+    if p.max_chunk > 0:
+        Lc = min(Lc, p.max_chunk)
+
+    items = []   # (r, h, row_lo, row_hi, kv_lo, kv_hi, slot)
+    merges = []  # (r, h, row_lo, row_hi, first_slot, n)
+    next_slot = 0
+    for (r, h, row_lo, row_hi, lo, hi, sink_hi) in units:
+        chunks = [(max(lo, k * Lc), min(hi, (k + 1) * Lc)) for k in range(lo // Lc, (hi - 1) // Lc + 1)]
+        if sink_hi > 0:
+            chunks.append((0, sink_hi))
+        if len(chunks) >= 2:
+            first = next_slot
+            next_slot += len(chunks)
+            merges.append((r, h, row_lo, row_hi, first, len(chunks)))
+            for c, (a, b) in enumerate(chunks):
+                items.append((r, h, row_lo, row_hi, a, b, first + c))
+        else:
+            a, b = chunks[0]
+            items.append((r, h, row_lo, row_hi, a, b, -1))
+
+    cost = [(it[5] - it[4]) + p.item_overhead for it in items]
+    order = sorted(range(len(items)), key=lambda i: (-cost[i], i))
+    heap = [(0, w) for w in range(W)]
+    heapq.heapify(heap)
+    worker_items = [[] for _ in range(W)]
+    load = [0] * W
+    for i in order:
+        ld, w = heapq.heappop(heap)
+        worker_items[w].append(i)
+        load[w] = ld + cost[i]
+        heapq.heappush(heap, (load[w], w))
+
+    if any(len(x) > p.max_items_per_worker for x in worker_items):
+        raise PlanError("CAPACITY", "too many items on one worker")
+    if next_slot > p.max_slots:
+        raise PlanError("CAPACITY", "too many partial-state slots")
+    if len(merges) > p.max_merge:
+        raise PlanError("CAPACITY", "too many merge entries")
+
+    return {
+        "group": g,
+        "units": np.asarray(units, dtype=np.int64).reshape(-1, 7),
+        "total_cost": C,
+        "chunk": Lc,
+        "items": np.asarray(items, dtype=np.int64).reshape(-1, 7),
+        "cost": np.asarray(cost, dtype=np.int64),
+        "worker_items": worker_items,
+        "load": np.asarray(load, dtype=np.int64),
+        "merge": np.asarray(merges, dtype=np.int64).reshape(-1, 6),
+        "num_slots": next_slot,
+    }
