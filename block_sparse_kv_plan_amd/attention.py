@@ -1,0 +1,126 @@
+"""plan/run wrapper over the C ABI, in the shape of a serving engine's batch
+attention object: ``plan()`` once per step from host lengths, then ``run()``
+(fixed launches, graph-capturable) for every layer.  torch provides device
+memory, pinned host memory and streams; all compute is in libbsk's kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import (DTYPE_BF16, DTYPE_F32, KV_DENSE, KV_PAGED, ROPE_NONE, TILE_DECODE, TILE_PREFILL, PlanInfo,
+               Problem, Tensors, device_workers, merge_state_pair, merge_states, plan, run_decode, run_prefill,
+               workspace_query)
+
+TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
+
+# Plan defaults per query-tile class: (tile_kv, split_factor, min_chunk, max_items_per_worker)
+DEFAULTS = {
+    TILE_DECODE: dict(tile_kv=16, split_factor=2, min_chunk=128, max_items_per_worker=64),
+    TILE_PREFILL: dict(tile_kv=64, split_factor=1, min_chunk=256, max_items_per_worker=64),
+}
+
+
+def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE_F32, kv_mode=KV_PAGED,
+                 page_size=16, causal=False, window=0, sink=0, rope_mode=ROPE_NONE, rope_theta=10000.0,
+                 sm_scale=None, tile_q=TILE_DECODE, num_workers, tile_kv=None, split_factor=None,
+                 min_chunk=None, max_chunk=0, item_overhead=0, max_batch, max_items_per_worker=None,
+                 max_slots=None, max_merge=None) -> Problem:
+    d = DEFAULTS[tile_q]
+    tile_kv = tile_kv if tile_kv is not None else max(d["tile_kv"], page_size if kv_mode == KV_PAGED else 1)
+    kmax = max_items_per_worker if max_items_per_worker is not None else d["max_items_per_worker"]
+    p = Problem()
+    p.num_qo_heads, p.num_kv_heads, p.head_dim = num_qo_heads, num_kv_heads, head_dim
+    p.dtype, p.out_dtype, p.kv_mode, p.page_size = dtype, out_dtype, kv_mode, page_size
+    p.causal, p.window, p.sink = int(causal), int(window), int(sink)
+    p.rope_mode, p.rope_theta = rope_mode, float(rope_theta)
+    p.sm_scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(head_dim))
+    p.tile_q, p.tile_kv, p.num_workers = tile_q, tile_kv, num_workers
+    p.split_factor = split_factor if split_factor is not None else d["split_factor"]
+    mc = min_chunk if min_chunk is not None else d["min_chunk"]
+    p.min_chunk = max(tile_kv, (mc // tile_kv) * tile_kv)
+    p.max_chunk, p.item_overhead = max_chunk, item_overhead
+    p.max_batch, p.max_items_per_worker = max_batch, kmax
+    p.max_slots = max_slots if max_slots is not None else num_workers * kmax
+    p.max_merge = max_merge if max_merge is not None else num_workers * kmax
+    return p
+
+
+def tensors_for(problem: Problem, q, k, v, out, lse, page_indices=None, layout: str = "HND", rope=None) -> Tensors:
+    """Describe torch tensors to the C ABI.  PAGED k/v: [pages, Hk, ps, d] ("HND") or
+    [pages, ps, Hk, d] ("NHD"); DENSE k/v: [N, Hk, d].  q/out: [T, Hq, d]; lse: [T, Hq]."""
+    t = Tensors()
+    t.q, t.q_stride_tok, t.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
+    t.k, t.v = k.data_ptr(), v.data_ptr()
+    if problem.kv_mode == KV_PAGED:
+        if layout == "HND":
+            t.k_stride_page, t.k_stride_head, t.k_stride_tok = k.stride(0), k.stride(1), k.stride(2)
+            t.v_stride_page, t.v_stride_head, t.v_stride_tok = v.stride(0), v.stride(1), v.stride(2)
+        elif layout == "NHD":
+            t.k_stride_page, t.k_stride_tok, t.k_stride_head = k.stride(0), k.stride(1), k.stride(2)
+            t.v_stride_page, t.v_stride_tok, t.v_stride_head = v.stride(0), v.stride(1), v.stride(2)
+        else:
+            raise ValueError(layout)
+        t.kv_page_indices = page_indices.data_ptr()
+    else:
+        t.k_stride_page, t.k_stride_tok, t.k_stride_head = 0, k.stride(0), k.stride(1)
+        t.v_stride_page, t.v_stride_tok, t.v_stride_head = 0, v.stride(0), v.stride(1)
+    for x in (q, k, v, out):
+        assert x.stride(-1) == 1, "last dimension must be contiguous"
+    t.out, t.o_stride_tok, t.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
+    t.lse, t.lse_stride_tok = lse.data_ptr(), lse.stride(0)
+    if rope is not None:
+        t.rope_cos_sin, t.rope_n_pos = rope.data_ptr(), rope.shape[0]
+    return t
+
+
+class BatchAttention:
+    """Owns the workspaces of one problem; plan() per step, run() per layer."""
+
+    def __init__(self, problem: Problem, device="cuda"):
+        self.problem = problem
+        int_b, float_b, host_b = workspace_query(problem)
+        self.device = torch.device(device)
+        self.int_ws = torch.empty(int_b, dtype=torch.uint8, device=self.device)
+        self.float_ws = torch.empty(max(float_b, 16), dtype=torch.uint8, device=self.device)
+        self.host_ws = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
+        self.info: Optional[PlanInfo] = None
+        self._upload_done = None
+
+    @classmethod
+    def create(cls, *, device="cuda", num_workers=None, **kw):
+        if num_workers is None:
+            num_workers = device_workers(kw.get("tile_q", TILE_DECODE), kw["head_dim"], kw["dtype"])
+        return cls(make_problem(num_workers=num_workers, **kw), device=device)
+
+    def plan(self, qo_indptr, kv_len, kv_indptr, stream=None) -> PlanInfo:
+        if self._upload_done is not None:
+            self._upload_done.synchronize()  # the previous plan's copy still reads host_ws
+        stream = stream or torch.cuda.current_stream(self.device)
+        self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
+                         self.host_ws, self.int_ws, stream)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        self._upload_done = ev
+        return self.info
+
+    def run(self, tensors: Tensors, stream=None, merge: bool = True):
+        stream = stream or torch.cuda.current_stream(self.device)
+        if self.problem.tile_q == TILE_DECODE:
+            run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        else:
+            run_prefill(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        if merge:
+            merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+
+
+def merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
+    """Row-wise state merge of two complete (O f32 [..., d], LSE f32 [...]) states."""
+    rows = lse_a.numel()
+    d = o_a.shape[-1]
+    out_dtype = DTYPE_BF16 if o_out.dtype == torch.bfloat16 else DTYPE_F32
+    merge_state_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, d, out_dtype,
+                     stream or torch.cuda.current_stream(o_a.device))

@@ -1,0 +1,54 @@
+// Launch-argument structs and constants shared by host dispatch and kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace bsk {
+
+constexpr int kWave = 64;
+constexpr int kMaxPages = 1024;  // page ids one work item may stage in LDS
+
+// Launch arguments of the attention kernels.  They depend only on the
+// problem, the tensors and the workspace addresses -- never on the plan's
+// contents -- so one capture of a launch stays valid across plans.
+struct AttnArgs {
+  const void* q;
+  int64_t q_st, q_sh;
+  const void* k;
+  const void* v;
+  int64_t k_sp, k_sh, k_st;
+  int64_t v_sp, v_sh, v_st;
+  const int32_t* page_indices;
+  void* out;
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t lse_st;
+  float* part_o;    // [slots][tile_q][D]
+  float* part_lse;  // [slots][tile_q]
+  const int32_t* ws;
+  const float* rope;  // [n_pos][D/2][2]
+  int32_t rope_n_pos;
+  int32_t group;
+  int32_t page_shift;
+  int32_t causal;
+  int32_t window;
+  int32_t sink;
+  int32_t out_bf16;
+  float scale_log2;  // sm_scale * log2(e): logits are kept in base 2
+};
+
+struct MergeArgs {
+  const int32_t* ws;
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t lse_st;
+  int32_t group;
+  int32_t out_bf16;
+};
+
+}  // namespace bsk

@@ -1,0 +1,367 @@
+// C ABI of libbsk: argument validation, plan upload and kernel dispatch.
+// The entry points and their contracts are declared in include/bsk.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "../../include/bsk.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+bsk_status fail(bsk_status code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+bsk_status hip_fail(hipError_t e, const char* what) {
+  return fail(BSK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest chunk (keys) whose page ids fit the kernels' LDS page list.
+int32_t kernel_chunk_cap(const bsk_problem& p) {
+  if (p.kv_mode == BSK_KV_DENSE) return 0;
+  const int64_t cap = int64_t(bsk::kMaxPages) * p.page_size;
+  return int32_t(std::min<int64_t>(cap / p.tile_kv * p.tile_kv, INT32_MAX / 2));
+}
+
+bsk_status check_problem(const bsk_problem* p) {
+  if (!p) return fail(BSK_ERR_INVALID_ARG, "problem is NULL");
+  if (p->num_qo_heads <= 0 || p->num_kv_heads <= 0 || p->num_qo_heads % p->num_kv_heads != 0)
+    return fail(BSK_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(BSK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (p->dtype != BSK_DTYPE_F32 && p->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "dtype");
+  if (p->out_dtype != BSK_DTYPE_F32 && p->out_dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "out_dtype");
+  if (p->kv_mode != BSK_KV_PAGED && p->kv_mode != BSK_KV_DENSE) return fail(BSK_ERR_INVALID_ARG, "kv_mode");
+  if (p->kv_mode == BSK_KV_PAGED && (!is_pow2(p->page_size) || p->page_size > 65536))
+    return fail(BSK_ERR_INVALID_ARG, "page_size must be a power of two <= 65536");
+  if (p->causal != 0 && p->causal != 1) return fail(BSK_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->window > 0 && p->sink < 0) return fail(BSK_ERR_INVALID_ARG, "sink must be >= 0");
+  if (p->rope_mode < BSK_ROPE_NONE || p->rope_mode > BSK_ROPE_ABSOLUTE) return fail(BSK_ERR_INVALID_ARG, "rope_mode");
+  if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
+    return fail(BSK_ERR_INVALID_ARG, "streaming RoPE positions need causal masking");
+  if (p->rope_mode != BSK_ROPE_NONE && !(p->rope_theta > 1.0)) return fail(BSK_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!std::isfinite(p->sm_scale)) return fail(BSK_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (p->tile_q != BSK_TILE_DECODE && p->tile_q != BSK_TILE_PREFILL)
+    return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 (decode) or 128 (prefill)");
+  if (p->tile_kv <= 0 || (p->kv_mode == BSK_KV_PAGED && p->tile_kv % p->page_size != 0))
+    return fail(BSK_ERR_INVALID_ARG, "tile_kv must be a positive multiple of page_size");
+  if (p->num_workers <= 0 || p->split_factor <= 0) return fail(BSK_ERR_INVALID_ARG, "num_workers, split_factor");
+  if (p->min_chunk <= 0 || p->min_chunk % p->tile_kv) return fail(BSK_ERR_INVALID_ARG, "min_chunk");
+  if (p->max_batch < 0 || p->max_items_per_worker <= 0 || p->max_slots < 0 || p->max_merge < 0)
+    return fail(BSK_ERR_INVALID_ARG, "capacities");
+  const int32_t cap = kernel_chunk_cap(*p);
+  if (cap > 0) {
+    if (p->max_chunk > cap) return fail(BSK_ERR_INVALID_ARG, "max_chunk exceeds the kernels' page-list capacity");
+    if (p->min_chunk > cap) return fail(BSK_ERR_INVALID_ARG, "min_chunk exceeds the kernels' page-list capacity");
+    if (p->window > 0 && int64_t(p->sink) > int64_t(bsk::kMaxPages) * p->page_size)
+      return fail(BSK_ERR_INVALID_ARG, "sink range exceeds the kernels' page-list capacity");
+  }
+  return BSK_OK;
+}
+
+bsk::PlanParams plan_params(const bsk_problem& p) {
+  bsk::PlanParams q;
+  q.num_qo_heads = p.num_qo_heads;
+  q.num_kv_heads = p.num_kv_heads;
+  q.tile_q = p.tile_q;
+  q.tile_kv = p.tile_kv;
+  q.num_workers = p.num_workers;
+  q.split_factor = p.split_factor;
+  q.min_chunk = p.min_chunk;
+  q.max_chunk = p.max_chunk > 0 ? p.max_chunk : kernel_chunk_cap(p);
+  q.item_overhead = p.item_overhead;
+  q.max_batch = p.max_batch;
+  q.max_items_per_worker = p.max_items_per_worker;
+  q.max_slots = p.max_slots;
+  q.max_merge = p.max_merge;
+  q.causal = p.causal != 0;
+  q.window = p.window > 0 ? p.window : 0;
+  q.sink = p.window > 0 ? p.sink : 0;
+  return q;
+}
+
+size_t float_ws_need(const bsk_problem& p) {
+  return size_t(p.max_slots) * size_t(p.tile_q) * size_t(p.head_dim + 1) * sizeof(float);
+}
+
+bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_tensors* t, const void* int_ws,
+                     void* float_ws, size_t float_ws_bytes, int tile_q) {
+  bsk_status s = check_problem(p);
+  if (s != BSK_OK) return s;
+  if (!info || !t || !int_ws) return fail(BSK_ERR_INVALID_ARG, "plan info, tensors and int workspace are required");
+  if (p->tile_q != tile_q || info->tile_q != tile_q)
+    return fail(BSK_ERR_INVALID_ARG, "plan was built for the other query-tile class");
+  if (info->num_workers != p->num_workers) return fail(BSK_ERR_INVALID_ARG, "plan info does not match problem");
+  if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*p)))
+    return fail(BSK_ERR_WORKSPACE, "float workspace smaller than bsk_workspace_query");
+  const size_t ebytes = p->dtype == BSK_DTYPE_BF16 ? 2 : 4;
+  const int64_t vec = 16 / int64_t(ebytes);
+  if (!t->q || !t->k || !t->v || !t->out || !t->lse) return fail(BSK_ERR_INVALID_ARG, "null tensor");
+  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16))
+    return fail(BSK_ERR_INVALID_ARG, "q, k, v must be 16-byte aligned");
+  if (t->q_stride_tok % vec || t->q_stride_head % vec || t->k_stride_head % vec || t->k_stride_tok % vec ||
+      t->v_stride_head % vec || t->v_stride_tok % vec ||
+      (p->kv_mode == BSK_KV_PAGED && (t->k_stride_page % vec || t->v_stride_page % vec)))
+    return fail(BSK_ERR_INVALID_ARG, "q/k/v strides must be multiples of 16 bytes");
+  if (!aligned(t->out, p->out_dtype == BSK_DTYPE_F32 ? 16 : 8) || t->o_stride_tok % 4 || t->o_stride_head % 4)
+    return fail(BSK_ERR_INVALID_ARG, "out must be aligned to 4 elements (strides too)");
+  if (p->kv_mode == BSK_KV_PAGED && !t->kv_page_indices) return fail(BSK_ERR_INVALID_ARG, "kv_page_indices is NULL");
+  if (p->rope_mode != BSK_ROPE_NONE) {
+    if (!t->rope_cos_sin || !aligned(t->rope_cos_sin, 16)) return fail(BSK_ERR_INVALID_ARG, "rope table missing");
+    int64_t need = info->max_kv_len;
+    if (p->rope_mode == BSK_ROPE_STREAMING && p->window > 0)
+      need = std::min<int64_t>(need, int64_t(p->window) + p->sink);
+    if (t->rope_n_pos < need) return fail(BSK_ERR_INVALID_ARG, "rope table has too few positions");
+    if (p->rope_mode == BSK_ROPE_STREAMING && info->max_qo_len > 1)
+      return fail(BSK_ERR_UNSUPPORTED, "streaming RoPE positions are per query; needs qo_len <= 1");
+  }
+  return BSK_OK;
+}
+
+bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* int_ws, void* float_ws) {
+  bsk::AttnArgs a;
+  a.q = t.q;
+  a.q_st = t.q_stride_tok;
+  a.q_sh = t.q_stride_head;
+  a.k = t.k;
+  a.v = t.v;
+  a.k_sp = t.k_stride_page;
+  a.k_sh = t.k_stride_head;
+  a.k_st = t.k_stride_tok;
+  a.v_sp = t.v_stride_page;
+  a.v_sh = t.v_stride_head;
+  a.v_st = t.v_stride_tok;
+  a.page_indices = t.kv_page_indices;
+  a.out = t.out;
+  a.o_st = t.o_stride_tok;
+  a.o_sh = t.o_stride_head;
+  a.lse = t.lse;
+  a.lse_st = t.lse_stride_tok;
+  float* fw = static_cast<float*>(float_ws);
+  a.part_o = fw;
+  a.part_lse = fw ? fw + size_t(p.max_slots) * p.tile_q * p.head_dim : nullptr;
+  a.ws = static_cast<const int32_t*>(int_ws);
+  a.rope = t.rope_cos_sin;
+  a.rope_n_pos = t.rope_n_pos;
+  a.group = p.num_qo_heads / p.num_kv_heads;
+  a.page_shift = p.kv_mode == BSK_KV_PAGED ? ilog2(p.page_size) : 0;
+  a.causal = p.causal;
+  a.window = p.window > 0 ? p.window : 0;
+  a.sink = p.window > 0 ? p.sink : 0;
+  a.out_bf16 = p.out_dtype == BSK_DTYPE_BF16;
+  a.scale_log2 = float(double(p.sm_scale) * 1.4426950408889634);
+  return a;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char* bsk_status_string(bsk_status status) {
+  switch (status) {
+    case BSK_OK: return "BSK_OK";
+    case BSK_ERR_INVALID_ARG: return "BSK_ERR_INVALID_ARG";
+    case BSK_ERR_UNSUPPORTED: return "BSK_ERR_UNSUPPORTED";
+    case BSK_ERR_CAPACITY: return "BSK_ERR_CAPACITY";
+    case BSK_ERR_WORKSPACE: return "BSK_ERR_WORKSPACE";
+    case BSK_ERR_HIP: return "BSK_ERR_HIP";
+    default: return "BSK_ERR_UNKNOWN";
+  }
+}
+
+const char* bsk_last_error(void) { return g_err.c_str(); }
+
+bsk_status bsk_device_workers(int32_t tile_q, int32_t head_dim, int32_t dtype, int32_t* num_workers) {
+  if (!num_workers) return fail(BSK_ERR_INVALID_ARG, "num_workers is NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(BSK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const void* fn = nullptr;
+  int threads = 0;
+  if (tile_q == BSK_TILE_DECODE) {
+    fn = bsk::decode_kernel_for_occupancy(dtype, head_dim);
+    threads = bsk::decode_threads();
+  } else if (tile_q == BSK_TILE_PREFILL) {
+    if (dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
+    fn = bsk::prefill_kernel_for_occupancy(head_dim);
+    threads = bsk::prefill_threads();
+  } else {
+    return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 or 128");
+  }
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  *num_workers = cus * (per_cu > 0 ? per_cu : 1);
+  return BSK_OK;
+}
+
+bsk_status bsk_workspace_query(const bsk_problem* problem, size_t* int_ws_bytes, size_t* float_ws_bytes,
+                               size_t* host_ws_bytes) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  const size_t ib = bsk::plan_workspace_bytes(plan_params(*problem));
+  if (int_ws_bytes) *int_ws_bytes = ib;
+  if (host_ws_bytes) *host_ws_bytes = ib;
+  if (float_ws_bytes) *float_ws_bytes = float_ws_need(*problem);
+  return BSK_OK;
+}
+
+bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo_indptr, const int32_t* kv_len,
+                    const int32_t* kv_indptr, void* host_ws, size_t host_ws_bytes, void* int_ws_dev,
+                    size_t int_ws_bytes, void* stream, bsk_plan_info* info) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (!info) return fail(BSK_ERR_INVALID_ARG, "info is NULL");
+  const bsk::PlanParams pp = plan_params(*problem);
+  if (problem->kv_mode == BSK_KV_PAGED && batch > 0 && kv_indptr && kv_len) {
+    for (int32_t r = 0; r < batch; ++r) {
+      const int64_t pages = int64_t(kv_indptr[r + 1]) - kv_indptr[r];
+      if (pages < 0 || int64_t(kv_len[r]) > pages * problem->page_size)
+        return fail(BSK_ERR_INVALID_ARG, "request " + std::to_string(r) + " has fewer pages than kv_len needs");
+    }
+  }
+  if (int_ws_dev && int_ws_bytes < bsk::plan_workspace_bytes(pp))
+    return fail(BSK_ERR_WORKSPACE, "int workspace smaller than bsk_workspace_query");
+  bsk::PlanStats st;
+  std::string err;
+  const bsk::PlanResult pr = bsk::build_plan(pp, batch, qo_indptr, kv_len, kv_indptr, static_cast<int32_t*>(host_ws),
+                                             host_ws_bytes, &st, &err);
+  if (pr == bsk::PLAN_CAPACITY) return fail(BSK_ERR_CAPACITY, err);
+  if (pr == bsk::PLAN_WORKSPACE) return fail(BSK_ERR_WORKSPACE, err);
+  if (pr != bsk::PLAN_OK) return fail(BSK_ERR_INVALID_ARG, err);
+  std::memset(info, 0, sizeof(*info));
+  info->num_workers = problem->num_workers;
+  info->tile_q = problem->tile_q;
+  info->batch = batch;
+  info->num_items = st.num_items;
+  info->num_slots = st.num_slots;
+  info->num_merge = st.num_merge;
+  info->chunk = st.chunk;
+  info->max_kv_len = st.max_kv_len;
+  info->max_qo_len = st.max_qo_len;
+  info->max_items_on_worker = st.max_items_on_worker;
+  info->total_cost = st.total_cost;
+  info->max_load = st.max_load;
+  info->used_bytes = st.used_bytes;
+  if (int_ws_dev) {
+    hipError_t e = hipMemcpyAsync(int_ws_dev, host_ws, size_t(st.used_bytes), hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  }
+  return BSK_OK;
+}
+
+bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                          const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
+  bsk_status s = check_run(problem, info, t, int_ws_dev, float_ws, float_ws_bytes, BSK_TILE_DECODE);
+  if (s != BSK_OK) return s;
+  if (problem->rope_mode != BSK_ROPE_NONE && problem->dtype != BSK_DTYPE_BF16)
+    return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for bf16 only");
+  if (problem->rope_mode != BSK_ROPE_NONE && problem->kv_mode != BSK_KV_PAGED)
+    return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for the paged layout only");
+  const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
+  hipError_t e = bsk::launch_decode(problem->dtype, problem->head_dim, problem->kv_mode == BSK_KV_DENSE,
+                                    problem->rope_mode, a, info->num_workers, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return BSK_OK;
+}
+
+bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                           const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
+  bsk_status s = check_run(problem, info, t, int_ws_dev, float_ws, float_ws_bytes, BSK_TILE_PREFILL);
+  if (s != BSK_OK) return s;
+  if (problem->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
+  if (problem->rope_mode != BSK_ROPE_NONE) return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for decode only");
+  const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
+  hipError_t e = bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, a, info->num_workers,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return BSK_OK;
+}
+
+bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                            const void* int_ws_dev, const void* float_ws, void* stream) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (!info || !t || !int_ws_dev || !t->out || !t->lse) return fail(BSK_ERR_INVALID_ARG, "null argument");
+  if (info->num_slots > 0 && !float_ws) return fail(BSK_ERR_INVALID_ARG, "float workspace is NULL");
+  if (!aligned(t->out, problem->out_dtype == BSK_DTYPE_F32 ? 16 : 8) || t->o_stride_tok % 4 || t->o_stride_head % 4)
+    return fail(BSK_ERR_INVALID_ARG, "out must be aligned to 4 elements (strides too)");
+  bsk::MergeArgs a;
+  a.ws = static_cast<const int32_t*>(int_ws_dev);
+  a.part_o = static_cast<const float*>(float_ws);
+  a.part_lse = float_ws ? a.part_o + size_t(problem->max_slots) * problem->tile_q * problem->head_dim : nullptr;
+  a.out = t->out;
+  a.o_st = t->o_stride_tok;
+  a.o_sh = t->o_stride_head;
+  a.lse = t->lse;
+  a.lse_st = t->lse_stride_tok;
+  a.group = problem->num_qo_heads / problem->num_kv_heads;
+  a.out_bf16 = problem->out_dtype == BSK_DTYPE_BF16;
+  int grid = problem->max_merge < 1 ? 1 : (problem->max_merge > 2048 ? 2048 : problem->max_merge);
+  hipError_t e = bsk::launch_merge(problem->head_dim, a, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return BSK_OK;
+}
+
+bsk_status bsk_merge_state_pair(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                                void* o_out, float* lse_out, int32_t rows, int32_t head_dim, int32_t out_dtype,
+                                void* stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return fail(BSK_ERR_INVALID_ARG, "null argument");
+  if (rows < 0 || head_dim <= 0 || head_dim % 4) return fail(BSK_ERR_INVALID_ARG, "rows / head_dim");
+  if (out_dtype != BSK_DTYPE_F32 && out_dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_INVALID_ARG, "out_dtype");
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o_out, out_dtype == BSK_DTYPE_F32 ? 16 : 8))
+    return fail(BSK_ERR_INVALID_ARG, "misaligned state arrays");
+  if (rows == 0) return BSK_OK;
+  hipError_t e = bsk::launch_merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, head_dim,
+                                        out_dtype == BSK_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge pair launch");
+  return BSK_OK;
+}
+
+bsk_status bsk_rope_table(float* table_dev, int32_t n_pos, int32_t head_dim, double theta, void* stream) {
+  if (!table_dev || n_pos <= 0 || head_dim <= 0 || head_dim % 2 || !(theta > 1.0))
+    return fail(BSK_ERR_INVALID_ARG, "rope table arguments");
+  hipError_t e = bsk::launch_rope_table(table_dev, n_pos, head_dim, theta, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return BSK_OK;
+}
+
+bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                            const void* int_ws_dev, const int64_t* row_offsets, void* k_out, void* v_out,
+                            void* stream) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (!info || !t || !int_ws_dev || !row_offsets || !k_out || !v_out || !t->k || !t->v)
+    return fail(BSK_ERR_INVALID_ARG, "null argument");
+  if (problem->kv_mode == BSK_KV_PAGED && !t->kv_page_indices) return fail(BSK_ERR_INVALID_ARG, "kv_page_indices");
+  const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, nullptr);
+  hipError_t e = bsk::launch_gather(problem->dtype, problem->head_dim, problem->kv_mode == BSK_KV_DENSE, a,
+                                    row_offsets, k_out, v_out, info->num_workers, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return BSK_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

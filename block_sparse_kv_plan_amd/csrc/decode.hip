@@ -1,0 +1,400 @@
+// Small-tile persistent attention kernel (16 query rows per work item).
+//
+// Serves decode -- query length 1, one row per q head of a GQA group, the
+// HBM-bound case of the FlashInfer 0.6 wiki ("Kernel types": Decode) -- and
+// short multi-token queries.  One workgroup is one persistent worker: it
+// walks its item list from the int workspace (FlashInfer paper summary,
+// "Research methodology" 3: the CPU plan cached on the GPU drives a fixed
+// launch).  Per item:
+//
+//   * the item's page ids are staged in LDS (FlashInfer 0.6 wiki,
+//     "Architecture" 1: page indices prefetched into shared memory);
+//   * the four waves take interleaved 16-key blocks of the item's key range;
+//     each lane loads 16-byte pieces of one key row, so a page's K (and V)
+//     rows are read as whole contiguous runs;
+//   * S^T = K Q^T on MFMA: the 16 keys are the M side and the (up to 16)
+//     query rows the N side, so every lane ends up owning one query row and
+//     four keys -- row max / sum need only two cross-lane steps;
+//   * online softmax in base 2 (log2 e folded into the scale);
+//   * O^T += V^T P^T on MFMA (bf16: V goes through a per-wave LDS buffer to
+//     be read key-major; f32: 16x16x4 MFMA reads V straight from memory);
+//   * the four waves' states are combined through LDS; a single-chunk item
+//     writes O and LSE, a chunk of a split unit writes its partial state.
+//
+// Fused RoPE (bf16): q and every key are rotated in fp32 with a cos/sin
+// table (the cache holds K unrotated), then split into bf16 hi + lo parts so
+// the MFMA logits keep ~16 significant bits: S = Kh.Qh + Kh.Ql + Kl.Qh.
+
+#include "device.h"
+#include "launch.h"
+
+namespace bsk {
+
+constexpr int kDecRows = 16;
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+
+enum : int { ROPE_NONE = 0, ROPE_STREAMING = 1, ROPE_ABSOLUTE = 2 };
+
+// Rotate-half RoPE on a lane's fragment pair: lo holds elements k..k+7 of
+// the first half, hi the matching k+D/2.. elements; cs points at the (cos,
+// sin) pairs of k..k+7 for the position.
+__device__ __forceinline__ void rope8(float* lo, float* hi, const float* __restrict__ cs) {
+  const float4* c4 = reinterpret_cast<const float4*>(cs);
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const float4 t = c4[e2];  // cos_e, sin_e, cos_e+1, sin_e+1
+    const int e = 2 * e2;
+    float x = lo[e], y = hi[e];
+    lo[e] = x * t.x - y * t.y;
+    hi[e] = y * t.x + x * t.y;
+    x = lo[e + 1];
+    y = hi[e + 1];
+    lo[e + 1] = x * t.z - y * t.w;
+    hi[e + 1] = y * t.z + x * t.w;
+  }
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const bf16x8& v, float* f) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf16_lo(u[e]);
+    f[2 * e + 1] = bf16_hi(u[e]);
+  }
+}
+
+// f (8 floats) -> hi = bf16(f), lo = bf16(f - hi)
+__device__ __forceinline__ void split_bf16x8(const float* f, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h0 = f32_to_bf16_bits(f[2 * e]);
+    const uint32_t h1 = f32_to_bf16_bits(f[2 * e + 1]);
+    h[e] = h0 | (h1 << 16);
+    l[e] = pack_bf16x2(f[2 * e] - __uint_as_float(h0 << 16), f[2 * e + 1] - __uint_as_float(h1 << 16));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+template <typename T, int D, bool DENSE, int ROPE>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(AttnArgs a) {
+  constexpr bool BF = __is_same(T, __bf16);
+  constexpr int NDB = D / 16;      // 16-wide output column blocks
+  constexpr int NKS = BF ? D / 32 : D / 4;  // MFMA k-steps over d for the logits
+  constexpr int HALF_KS = D / 64;  // bf16 k-step offset of the rotate-half partner
+  constexpr int VROW = D + 8;      // bf16 per row of the V buffer (padding spreads banks)
+  constexpr int AROW = D + 4;      // floats per row of the combine buffer
+  constexpr int V_BYTES = kDecWaves * 16 * VROW * 2;
+  constexpr int C_BYTES = kDecWaves * 16 * AROW * 4;
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(BF || ROPE == ROPE_NONE, "fused RoPE is built for bf16 only");
+
+  __shared__ __align__(16) unsigned char s_raw[V_BYTES > C_BYTES ? V_BYTES : C_BYTES];
+  __shared__ int32_t s_pages[DENSE ? 1 : kMaxPages];
+  __shared__ float s_m[kDecWaves][16];
+  __shared__ float s_l[kDecWaves][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int n = lane & 15;  // MFMA N index: this lane's query row; also its key row for loads
+  const int j = lane >> 4;  // lane group
+
+  const int32_t* __restrict__ ws = a.ws;
+  const int it_begin = ws[HDR_WORDS + blockIdx.x];
+  const int it_end = ws[HDR_WORDS + blockIdx.x + 1];
+  const int32_t* __restrict__ items = ws + ws[HDR_OFF_ITEMS];
+  const int32_t* __restrict__ qo_indptr = ws + ws[HDR_OFF_QO];
+  const int32_t* __restrict__ kv_lens = ws + ws[HDR_OFF_KVLEN];
+  const int32_t* __restrict__ kv_ind = ws + ws[HDR_OFF_KVIND];
+  const T* __restrict__ Qp = static_cast<const T*>(a.q);
+  const T* __restrict__ Kp = static_cast<const T*>(a.k);
+  const T* __restrict__ Vp = static_cast<const T*>(a.v);
+  const int g = a.group;
+
+  for (int it = it_begin; it < it_end; ++it) {
+    const int32_t* rec = items + int64_t(it) * ITEM_WORDS;
+    const int r = rec[IT_R], h = rec[IT_H];
+    const int row_lo = rec[IT_ROW_LO], row_hi = rec[IT_ROW_HI];
+    const int kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI];
+    const int slot = rec[IT_SLOT];
+    const int q0 = qo_indptr[r];
+    const int qlen = qo_indptr[r + 1] - q0;
+    const int L = kv_lens[r];
+    const int kbase = kv_ind[r];
+
+    if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, kDecThreads);
+    __syncthreads();
+
+    // ---- this lane's query row and its q fragment (MFMA B operand)
+    const int rho = row_lo + n;
+    const bool row_ok = rho < row_hi;
+    const int qi = row_ok ? rho / g : 0;
+    const int qu = row_ok ? rho % g : 0;
+    const int qpos = L - qlen + qi;
+    const T* qrow = Qp + int64_t(q0 + qi) * a.q_st + int64_t(h * g + qu) * a.q_sh;
+
+    // RoPE positions (see the key loop)
+    int lo_w = 0, n_s = 0;
+    if constexpr (ROPE == ROPE_STREAMING) {
+      lo_w = a.window > 0 ? max(0, qpos - a.window + 1) : 0;
+      n_s = a.window > 0 ? min(a.sink, lo_w) : 0;
+    }
+
+    bf16x8 qh[BF ? NKS : 1], ql[BF && ROPE != ROPE_NONE ? NKS : 1];
+    float qf[BF ? 1 : NKS];
+    if constexpr (BF) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        qh[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 8 * (4 * s + j)) : bf16x8{};
+      }
+      if constexpr (ROPE != ROPE_NONE) {
+        int pq = ROPE == ROPE_STREAMING ? n_s + (qpos - lo_w) : qpos;
+        pq = min(max(pq, 0), a.rope_n_pos - 1);
+#pragma unroll
+        for (int s = 0; s < HALF_KS; ++s) {
+          float lo[8], hi[8];
+          unpack_bf16x8(qh[s], lo);
+          unpack_bf16x8(qh[s + HALF_KS], hi);
+          rope8(lo, hi, a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2);
+          split_bf16x8(lo, qh[s], ql[s]);
+          split_bf16x8(hi, qh[s + HALF_KS], ql[s + HALF_KS]);
+        }
+        if (!row_ok) {
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) qh[s] = ql[s] = bf16x8{};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NKS; s += 4) {
+        const float4 x = row_ok ? *reinterpret_cast<const float4*>(qrow + j * (D / 4) + s) : float4{0, 0, 0, 0};
+        qf[s] = x.x;
+        qf[s + 1] = x.y;
+        qf[s + 2] = x.z;
+        qf[s + 3] = x.w;
+      }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0, 0, 0, 0};
+
+    unsigned short* s_v = reinterpret_cast<unsigned short*>(s_raw) + wave * 16 * VROW;
+    const int nblk = (kv_hi - kv_lo + 15) >> 4;
+    for (int b = wave; b < nblk; b += kDecWaves) {
+      const int tb = kv_lo + (b << 4);
+      const int tk = min(tb + n, kv_hi - 1);  // key row this lane loads (clamped: masked below)
+      const int64_t koff = kv_offset<DENSE>(s_pages, tk, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
+      const int64_t voff = kv_offset<DENSE>(s_pages, tk, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
+
+      f32x4 st = {0, 0, 0, 0};
+      bf16x8 vf[BF ? NKS : 1];
+      if constexpr (BF) {
+        bf16x8 kf[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(Kp + koff + 8 * (4 * s + j));
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) vf[s] = *reinterpret_cast<const bf16x8*>(Vp + voff + 8 * (4 * s + j));
+        if constexpr (ROPE == ROPE_NONE) {
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
+        } else {
+          int pk = ROPE == ROPE_STREAMING ? (tk < n_s ? tk : n_s + (tk - lo_w)) : tk;
+          pk = min(max(pk, 0), a.rope_n_pos - 1);
+          bf16x8 kl[NKS];
+#pragma unroll
+          for (int s = 0; s < HALF_KS; ++s) {
+            float lo[8], hi[8];
+            unpack_bf16x8(kf[s], lo);
+            unpack_bf16x8(kf[s + HALF_KS], hi);
+            rope8(lo, hi, a.rope + (int64_t(pk) * (D / 2) + 8 * (4 * s + j)) * 2);
+            split_bf16x8(lo, kf[s], kl[s]);
+            split_bf16x8(hi, kf[s + HALF_KS], kl[s + HALF_KS]);
+          }
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) {
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], ql[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[s], qh[s], st, 0, 0, 0);
+          }
+        }
+      } else {
+        float kf[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; s += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(Kp + koff + j * (D / 4) + s);
+          kf[s] = x.x;
+          kf[s + 1] = x.y;
+          kf[s + 2] = x.z;
+          kf[s + 3] = x.w;
+        }
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], qf[s], st, 0, 0, 0);
+      }
+
+      // mask + scale: st[i] is the logit of key tb + 4j + i for query row n
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tb + 4 * j + i;
+        const bool ok = row_ok && t < kv_hi && key_visible(t, qpos, a.causal, a.window, a.sink);
+        sv[i] = ok ? st[i] * a.scale_log2 : -INFINITY;
+      }
+      // online softmax (base 2)
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = wave_max_xor16_32(bm);
+      const float m_new = fmaxf(m_run, bm);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+      l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+
+      if constexpr (BF) {
+        // V rows -> per-wave LDS buffer, then read key-major for the A operand
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+          *reinterpret_cast<bf16x8*>(s_v + n * VROW + 8 * (4 * s + j)) = vf[s];
+        __builtin_amdgcn_wave_barrier();
+        u32x2 pw;
+        pw[0] = pack_bf16x2(p[0], p[1]);
+        pw[1] = pack_bf16x2(p[2], p[3]);
+        const i16x4 pb = __builtin_bit_cast(i16x4, pw);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          i16x4 va;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[e] = static_cast<short>(s_v[(4 * j + e) * VROW + 16 * db + n]);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tv = min(tb + 4 * j + i, kv_hi - 1);
+          const int64_t vo =
+              kv_offset<DENSE>(s_pages, tv, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(static_cast<float>(Vp[vo + 16 * db + n]), p[i], acc[db],
+                                                           0, 0, 0);
+        }
+      }
+    }
+
+    // ---- combine the four waves' states (acc^T: lane holds row n, columns 16db + 4j + i)
+    l_run = wave_sum_xor16_32(l_run);
+    if (j == 0) {
+      s_m[wave][n] = m_run;
+      s_l[wave][n] = l_run;
+    }
+    __syncthreads();
+    {
+      float M = fmaxf(fmaxf(s_m[0][n], s_m[1][n]), fmaxf(s_m[2][n], s_m[3][n]));
+      const float my = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      float* cacc = reinterpret_cast<float*>(s_raw) + (wave * 16 + n) * AROW;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<float4*>(cacc + 16 * db + 4 * j) =
+            float4{acc[db][0] * my, acc[db][1] * my, acc[db][2] * my, acc[db][3] * my};
+    }
+    __syncthreads();
+    const int nrows = row_hi - row_lo;
+    const float* cbase = reinterpret_cast<const float*>(s_raw);
+    for (int e = tid; e < nrows * (D / 4); e += kDecThreads) {
+      const int rr = e / (D / 4);
+      const int c4 = (e % (D / 4)) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+      float Lsum = 0.f;
+      float4 o = {0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        if (s_m[w][rr] != -INFINITY) Lsum += s_l[w][rr] * __builtin_amdgcn_exp2f(s_m[w][rr] - M);
+        const float4 x = *reinterpret_cast<const float4*>(cbase + (w * 16 + rr) * AROW + c4);
+        o.x += x.x;
+        o.y += x.y;
+        o.z += x.z;
+        o.w += x.w;
+      }
+      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      o.x *= inv;
+      o.y *= inv;
+      o.z *= inv;
+      o.w *= inv;
+      const float lse = Lsum > 0.f ? (M + __log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+      const int row = row_lo + rr;
+      if (slot < 0) {
+        const int tok = q0 + row / g;
+        const int qhd = h * g + row % g;
+        const int64_t oo = int64_t(tok) * a.o_st + int64_t(qhd) * a.o_sh + c4;
+        if (a.out_bf16) {
+          uint2 pk2 = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+          *reinterpret_cast<uint2*>(static_cast<__bf16*>(a.out) + oo) = pk2;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oo) = o;
+        }
+        if (c4 == 0) a.lse[int64_t(tok) * a.lse_st + qhd] = lse;
+      } else {
+        *reinterpret_cast<float4*>(a.part_o + (int64_t(slot) * kDecRows + rr) * D + c4) = o;
+        if (c4 == 0) a.part_lse[int64_t(slot) * kDecRows + rr] = lse;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- host launchers
+
+template <typename T, int D, bool DENSE, int ROPE>
+hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<T, D, DENSE, ROPE>), dim3(grid), dim3(kDecThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool DENSE, int ROPE>
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<T, D, DENSE, ROPE>);
+}
+
+// dtype: 0 f32, 1 bf16.  Returns hipErrorInvalidValue for combinations not built.
+hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, const AttnArgs& a, int grid,
+                         hipStream_t stream) {
+#define BSK_DEC(T, D, DN, R)                                                     \
+  if (head_dim == D && dense == DN && rope == R) return launch_one<T, D, DN, R>(a, grid, stream);
+  if (dtype == 1) {
+    BSK_DEC(__bf16, 128, false, ROPE_NONE)
+    BSK_DEC(__bf16, 128, true, ROPE_NONE)
+    BSK_DEC(__bf16, 64, false, ROPE_NONE)
+    BSK_DEC(__bf16, 64, true, ROPE_NONE)
+    BSK_DEC(__bf16, 128, false, ROPE_STREAMING)
+    BSK_DEC(__bf16, 128, false, ROPE_ABSOLUTE)
+    BSK_DEC(__bf16, 64, false, ROPE_STREAMING)
+    BSK_DEC(__bf16, 64, false, ROPE_ABSOLUTE)
+  } else {
+    BSK_DEC(float, 64, false, ROPE_NONE)
+    BSK_DEC(float, 64, true, ROPE_NONE)
+    BSK_DEC(float, 128, false, ROPE_NONE)
+    BSK_DEC(float, 128, true, ROPE_NONE)
+  }
+#undef BSK_DEC
+  return hipErrorInvalidValue;
+}
+
+const void* decode_kernel_for_occupancy(int dtype, int head_dim) {
+  if (dtype == 1) return head_dim == 64 ? kernel_ptr<__bf16, 64, false, ROPE_NONE>() : kernel_ptr<__bf16, 128, false, ROPE_NONE>();
+  return head_dim == 64 ? kernel_ptr<float, 64, false, ROPE_NONE>() : kernel_ptr<float, 128, false, ROPE_NONE>();
+}
+
+int decode_threads() { return kDecThreads; }
+
+}  // namespace bsk

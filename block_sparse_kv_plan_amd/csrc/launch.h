@@ -1,0 +1,26 @@
+// Host-side launchers of the device kernels (defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "args.h"
+
+namespace bsk {
+
+hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, const AttnArgs& a, int grid,
+                         hipStream_t stream);
+const void* decode_kernel_for_occupancy(int dtype, int head_dim);
+int decode_threads();
+
+hipError_t launch_prefill(int head_dim, bool dense, const AttnArgs& a, int grid, hipStream_t stream);
+const void* prefill_kernel_for_occupancy(int head_dim);
+int prefill_threads();
+
+hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t stream);
+hipError_t launch_merge_pair(const float* oa, const float* la, const float* ob, const float* lb, void* out,
+                             float* lse_out, int rows, int D, int out_bf16, hipStream_t stream);
+hipError_t launch_rope_table(float* table, int n_pos, int D, double theta, hipStream_t stream);
+hipError_t launch_gather(int dtype, int head_dim, bool dense, const AttnArgs& a, const int64_t* row_off, void* k_out,
+                         void* v_out, int grid, hipStream_t stream);
+
+}  // namespace bsk

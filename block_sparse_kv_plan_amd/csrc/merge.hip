@@ -1,0 +1,203 @@
+// Partial-state merge, RoPE table and the gather test hook.
+//
+// Split-KV (FlashInfer 0.6 wiki, "Kernel types": the split_kv decode path)
+// leaves one (O_c, LSE_c) per key chunk; the exact combination is
+//   M = max_c LSE_c,  LSE = M + ln sum_c exp(LSE_c - M),
+//   O = sum_c exp(LSE_c - LSE) O_c,
+// with every chunk empty (LSE_c = -inf) giving O = 0, LSE = -inf.  The
+// composable format (FlashInfer paper summary, "Research methodology" 1)
+// uses the same combination for a dense-prefix state and a paged-suffix
+// state.
+
+#include "device.h"
+#include "launch.h"
+
+namespace bsk {
+
+constexpr int kMergeThreads = 256;
+
+// Plan-driven merge: fixed grid; block b takes merge entries b, b + grid, ...
+// Threads cover (row, 4 columns) pairs of an entry.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  const int32_t* __restrict__ ws = a.ws;
+  const int n_merge = ws[HDR_NUM_MERGE];
+  const int tile_q = ws[HDR_TILE_Q];
+  const int32_t* __restrict__ table = ws + ws[HDR_OFF_MERGE];
+  const int32_t* __restrict__ qo_indptr = ws + ws[HDR_OFF_QO];
+  const int g = a.group;
+  for (int m = blockIdx.x; m < n_merge; m += gridDim.x) {
+    const int32_t* rec = table + int64_t(m) * MERGE_WORDS;
+    const int r = rec[MG_R], h = rec[MG_H], row_lo = rec[MG_ROW_LO], row_hi = rec[MG_ROW_HI];
+    const int first = rec[MG_FIRST_SLOT], nc = rec[MG_N];
+    const int q0 = qo_indptr[r];
+    const int nrows = row_hi - row_lo;
+    for (int e = threadIdx.x; e < nrows * (D / 4); e += kMergeThreads) {
+      const int rr = e / (D / 4);
+      const int c4 = (e % (D / 4)) * 4;
+      float M = -INFINITY;
+      for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[int64_t(first + c) * tile_q + rr]);
+      float4 o = {0, 0, 0, 0};
+      float lse = -INFINITY;
+      if (M != -INFINITY) {
+        float wsum = 0.f;
+        for (int c = 0; c < nc; ++c) wsum += __expf(a.part_lse[int64_t(first + c) * tile_q + rr] - M);
+        lse = M + __logf(wsum);
+        for (int c = 0; c < nc; ++c) {
+          const int64_t s = int64_t(first + c) * tile_q + rr;
+          const float w = __expf(a.part_lse[s] - lse);
+          const float4 x = *reinterpret_cast<const float4*>(a.part_o + s * D + c4);
+          o.x += w * x.x;
+          o.y += w * x.y;
+          o.z += w * x.z;
+          o.w += w * x.w;
+        }
+      }
+      const int row = row_lo + rr;
+      const int tok = q0 + row / g;
+      const int qhd = h * g + row % g;
+      const int64_t oo = int64_t(tok) * a.o_st + int64_t(qhd) * a.o_sh + c4;
+      if (a.out_bf16) {
+        uint2 pk2 = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+        *reinterpret_cast<uint2*>(static_cast<__bf16*>(a.out) + oo) = pk2;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oo) = o;
+      }
+      if (c4 == 0) a.lse[int64_t(tok) * a.lse_st + qhd] = lse;
+    }
+  }
+}
+
+// Row-wise merge of two complete states (composable prefix + suffix).
+__global__ __launch_bounds__(kMergeThreads) void merge_pair_kernel(const float* __restrict__ oa,
+                                                                   const float* __restrict__ la,
+                                                                   const float* __restrict__ ob,
+                                                                   const float* __restrict__ lb, void* out,
+                                                                   float* lse_out, int rows, int D, int out_bf16) {
+  const int per_row = D / 4;
+  const int64_t total = int64_t(rows) * per_row;
+  for (int64_t e = blockIdx.x * int64_t(kMergeThreads) + threadIdx.x; e < total;
+       e += int64_t(gridDim.x) * kMergeThreads) {
+    const int64_t row = e / per_row;
+    const int c4 = int(e % per_row) * 4;
+    const float x = la[row], y = lb[row];
+    const float M = fmaxf(x, y);
+    float4 o = {0, 0, 0, 0};
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+      const float ex = __expf(x - M), ey = __expf(y - M);
+      lse = M + __logf(ex + ey);
+      const float wa = __expf(x - lse), wb = __expf(y - lse);
+      const float4 p = *reinterpret_cast<const float4*>(oa + row * D + c4);
+      const float4 q = *reinterpret_cast<const float4*>(ob + row * D + c4);
+      o = float4{wa * p.x + wb * q.x, wa * p.y + wb * q.y, wa * p.z + wb * q.z, wa * p.w + wb * q.w};
+    }
+    if (out_bf16) {
+      uint2 pk2 = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+      *reinterpret_cast<uint2*>(static_cast<__bf16*>(out) + row * D + c4) = pk2;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + row * D + c4) = o;
+    }
+    if (c4 == 0) lse_out[row] = lse;
+  }
+}
+
+// table[p][k] = (cos, sin)(p * theta^(-2k/D)), evaluated in fp64.
+__global__ void rope_table_kernel(float* table, int n_pos, int D, double theta) {
+  const int half = D / 2;
+  const int64_t total = int64_t(n_pos) * half;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t p = e / half;
+    const int k = int(e % half);
+    const double inv_freq = pow(theta, -2.0 * double(k) / double(D));
+    const double ang = double(p) * inv_freq;
+    table[2 * e] = float(cos(ang));
+    table[2 * e + 1] = float(sin(ang));
+  }
+}
+
+// Test hook: copy every item's keys through the attention kernels' gather path.
+template <typename T, int D, bool DENSE>
+__global__ __launch_bounds__(256) void gather_kernel(AttnArgs a, const int64_t* __restrict__ row_off, T* kout,
+                                                     T* vout) {
+  __shared__ int32_t s_pages[DENSE ? 1 : kMaxPages];
+  const int32_t* __restrict__ ws = a.ws;
+  const int it_begin = ws[HDR_WORDS + blockIdx.x];
+  const int it_end = ws[HDR_WORDS + blockIdx.x + 1];
+  const int32_t* __restrict__ items = ws + ws[HDR_OFF_ITEMS];
+  const int32_t* __restrict__ kv_ind = ws + ws[HDR_OFF_KVIND];
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  for (int it = it_begin; it < it_end; ++it) {
+    const int32_t* rec = items + int64_t(it) * ITEM_WORDS;
+    const int r = rec[IT_R], h = rec[IT_H], kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI], id = rec[IT_ID];
+    const int kbase = kv_ind[r];
+    if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, threadIdx.x, 256);
+    __syncthreads();
+    const int64_t base = row_off[id];
+    for (int e = threadIdx.x; e < (kv_hi - kv_lo) * D; e += 256) {
+      const int t = kv_lo + e / D;
+      const int c = e % D;
+      const int64_t ko = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
+      const int64_t vo = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
+      kout[(base + (t - kv_lo)) * D + c] = K[ko + c];
+      vout[(base + (t - kv_lo)) * D + c] = V[vo + c];
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- host launchers
+
+hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t stream) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_pair(const float* oa, const float* la, const float* ob, const float* lb, void* out,
+                             float* lse_out, int rows, int D, int out_bf16, hipStream_t stream) {
+  const int64_t total = int64_t(rows) * (D / 4);
+  int grid = int((total + kMergeThreads - 1) / kMergeThreads);
+  grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);
+  hipLaunchKernelGGL(merge_pair_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, oa, la, ob, lb, out, lse_out,
+                     rows, D, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* table, int n_pos, int D, double theta, hipStream_t stream) {
+  const int64_t total = int64_t(n_pos) * (D / 2);
+  int grid = int((total + 255) / 256);
+  grid = grid < 1 ? 1 : (grid > 8192 ? 8192 : grid);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, stream, table, n_pos, D, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int dtype, int head_dim, bool dense, const AttnArgs& a, const int64_t* row_off, void* k_out,
+                         void* v_out, int grid, hipStream_t stream) {
+#define BSK_GATHER(T, D, DN)                                                                                     \
+  if (head_dim == D && dense == DN) {                                                                            \
+    hipLaunchKernelGGL((gather_kernel<T, D, DN>), dim3(grid), dim3(256), 0, stream, a, row_off,                  \
+                       static_cast<T*>(k_out), static_cast<T*>(v_out));                                          \
+    return hipGetLastError();                                                                                    \
+  }
+  if (dtype == 1) {
+    BSK_GATHER(__bf16, 128, false)
+    BSK_GATHER(__bf16, 128, true)
+    BSK_GATHER(__bf16, 64, false)
+    BSK_GATHER(__bf16, 64, true)
+  } else {
+    BSK_GATHER(float, 128, false)
+    BSK_GATHER(float, 128, true)
+    BSK_GATHER(float, 64, false)
+    BSK_GATHER(float, 64, true)
+  }
+#undef BSK_GATHER
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsk

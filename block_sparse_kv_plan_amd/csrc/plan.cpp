@@ -1,0 +1,278 @@
+// Host work planner for the persistent attention kernels.
+//
+// The FlashInfer paper summary ("Research methodology" 3, dynamic
+// load-balanced scheduling) describes the split this file implements:
+// query-tile sizes are fixed when the kernels are compiled, while the
+// runtime sequence lengths drive a CPU plan that spreads the work evenly
+// over all compute units; the plan is copied to the GPU and a fixed-size
+// launch runs it, so it stays compatible with graph capture.  The PR #5329
+// analysis ("Code analysis" 1) shows the persistent kernel taking its grid
+// from the plan and serving a 128-row and a 16-row query-tile class.
+//
+// The pages give no algorithm, so the plan is defined here, in integer
+// arithmetic with explicit tie-breaks (the test oracle implements the same
+// rules independently and must agree bit for bit):
+//
+//  1. Units: for each request r with qo_len > 0 and kv_len > 0, each kv
+//     head h and each query tile t.  Rows of a request are (token i, group
+//     member u) flattened as i*g + u; tile t covers rows
+//     [t*tile_q, min((t+1)*tile_q, qo_len*g)).  With i_lo/i_hi its first and
+//     last token and qpos(i) = kv_len - qo_len + i, the unit needs keys
+//     [lo, hi): hi = min(kv_len, qpos(i_hi) + 1) if causal else kv_len;
+//     lo = max(0, qpos(i_lo) - window + 1) if window > 0 else 0; plus the
+//     sink range [0, min(sink, lo)) when window > 0 and lo > 0.
+//  2. Total cost C = sum of (hi - lo) + |sink range| over units.
+//  3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W * split)), tile_kv)),
+//     then min(L_c, max_chunk) if max_chunk > 0.
+//  4. A unit's chunks: [max(lo, k L_c), min(hi, (k+1) L_c)) for
+//     k = lo / L_c .. (hi-1) / L_c, then the non-empty sink range.
+//  5. Items in unit order, then chunk order; id = creation index;
+//     cost = keys + item_overhead.  Units with >= 2 chunks take consecutive
+//     partial slots from a global counter; single-chunk units use slot -1.
+//  6. Longest-processing-time assignment: items sorted by (cost desc, id
+//     asc); a min-heap of (load, worker) starting at (0, w); each item pops
+//     the lexicographic minimum, is appended to that worker's list, and
+//     (load + cost, worker) is pushed back.
+//  7. Merge table: one entry per multi-chunk unit, in unit order.
+//  8. More than max_items_per_worker items on a worker, max_slots slots or
+//     max_merge entries is a capacity error (no fallback).
+
+#include "plan.h"
+
+#include <algorithm>
+#include <array>
+#include <cstring>
+#include <functional>
+#include <queue>
+#include <utility>
+#include <vector>
+
+#include "layout.h"
+
+namespace bsk {
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align4(int64_t x) { return (x + 3) & ~int64_t(3); }
+
+struct Layout {
+  int64_t off_items, off_merge, off_qo, off_kvlen, off_kvind, total_words;
+};
+
+// Word offsets for a plan with `n_items` items and `n_merge` merge entries.
+Layout layout_for(int32_t W, int64_t n_items, int64_t n_merge, int32_t batch) {
+  Layout L;
+  L.off_items = align4(HDR_WORDS + int64_t(W) + 1);
+  L.off_merge = L.off_items + n_items * ITEM_WORDS;
+  L.off_qo = L.off_merge + n_merge * MERGE_WORDS;
+  L.off_kvlen = L.off_qo + batch + 1;
+  L.off_kvind = L.off_kvlen + batch;
+  L.total_words = L.off_kvind + batch + 1;
+  return L;
+}
+
+struct Unit {
+  int32_t r, h, row_lo, row_hi, lo, hi, sink_hi;
+};
+
+}  // namespace
+
+size_t plan_workspace_bytes(const PlanParams& p) {
+  const int64_t max_items = int64_t(p.num_workers) * p.max_items_per_worker;
+  Layout L = layout_for(p.num_workers, max_items, p.max_merge, p.max_batch);
+  return size_t(L.total_words) * sizeof(int32_t);
+}
+
+PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indptr, const int32_t* kv_len,
+                      const int32_t* kv_indptr, int32_t* buf, size_t buf_bytes, PlanStats* stats,
+                      std::string* err) {
+  auto fail = [&](PlanResult code, const std::string& msg) {
+    if (err) *err = msg;
+    return code;
+  };
+  if (p.num_kv_heads <= 0 || p.num_qo_heads <= 0 || p.num_qo_heads % p.num_kv_heads != 0)
+    return fail(PLAN_INVALID, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (p.tile_q <= 0 || p.tile_kv <= 0 || p.num_workers <= 0 || p.split_factor <= 0)
+    return fail(PLAN_INVALID, "tile_q, tile_kv, num_workers and split_factor must be positive");
+  if (p.min_chunk <= 0 || p.min_chunk % p.tile_kv != 0)
+    return fail(PLAN_INVALID, "min_chunk must be a positive multiple of tile_kv");
+  if (p.max_chunk < 0 || (p.max_chunk > 0 && (p.max_chunk % p.tile_kv != 0 || p.max_chunk < p.min_chunk)))
+    return fail(PLAN_INVALID, "max_chunk must be 0 or a multiple of tile_kv that is >= min_chunk");
+  if (p.item_overhead < 0) return fail(PLAN_INVALID, "item_overhead must be >= 0");
+  if (batch < 0 || batch > p.max_batch) return fail(PLAN_INVALID, "batch must be in [0, max_batch]");
+  if (batch > 0 && (!qo_indptr || !kv_len || !kv_indptr)) return fail(PLAN_INVALID, "null length array");
+  if (!buf) return fail(PLAN_INVALID, "null host workspace");
+  if (buf_bytes < plan_workspace_bytes(p)) return fail(PLAN_WORKSPACE, "host workspace smaller than bsk_workspace_query");
+
+  const int32_t g = p.num_qo_heads / p.num_kv_heads;
+  const int32_t W = p.num_workers;
+  if (batch > 0 && qo_indptr[0] != 0) return fail(PLAN_INVALID, "qo_indptr[0] must be 0");
+  int32_t max_kv = 0, max_qo = 0;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t Q = int64_t(qo_indptr[r + 1]) - qo_indptr[r];
+    const int64_t L = kv_len[r];
+    if (Q < 0 || L < 0 || Q > L) return fail(PLAN_INVALID, "need 0 <= qo_len <= kv_len for every request");
+    if (kv_indptr[r + 1] < kv_indptr[r]) return fail(PLAN_INVALID, "kv_indptr must be non-decreasing");
+    if (Q * g > INT32_MAX) return fail(PLAN_INVALID, "too many query rows");
+    max_kv = std::max<int32_t>(max_kv, int32_t(L));
+    max_qo = std::max<int32_t>(max_qo, int32_t(Q));
+  }
+
+  // 1. units
+  std::vector<Unit> units;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int32_t Q = qo_indptr[r + 1] - qo_indptr[r];
+    const int32_t L = kv_len[r];
+    if (Q == 0 || L == 0) continue;
+    const int32_t rows = Q * g;
+    for (int32_t h = 0; h < p.num_kv_heads; ++h) {
+      for (int32_t t = 0; t < int32_t(ceil_div(rows, p.tile_q)); ++t) {
+        Unit u;
+        u.r = r;
+        u.h = h;
+        u.row_lo = t * p.tile_q;
+        u.row_hi = std::min(rows, (t + 1) * p.tile_q);
+        const int32_t qpos_lo = L - Q + u.row_lo / g;
+        const int32_t qpos_hi = L - Q + (u.row_hi - 1) / g;
+        u.hi = p.causal ? std::min(L, qpos_hi + 1) : L;
+        u.lo = p.window > 0 ? std::max(0, qpos_lo - p.window + 1) : 0;
+        u.sink_hi = (p.window > 0 && u.lo > 0) ? std::min(p.sink, u.lo) : 0;
+        units.push_back(u);
+      }
+    }
+  }
+
+  // 2-3. total cost and chunk length
+  int64_t C = 0;
+  for (const Unit& u : units) C += int64_t(u.hi - u.lo) + u.sink_hi;
+  int64_t Lc = ceil_div(ceil_div(C, int64_t(W) * p.split_factor), p.tile_kv) * p.tile_kv;
+  Lc = std::max<int64_t>(p.min_chunk, Lc);
+  if (p.max_chunk > 0) Lc = std::min<int64_t>(Lc, p.max_chunk);
+  if (Lc > INT32_MAX) return fail(PLAN_INVALID, "chunk length overflows int32");
+
+  // 4-5. chunks -> items, slots, merge entries
+  struct Item {
+    int32_t r, h, row_lo, row_hi, kv_lo, kv_hi, slot;
+    int64_t cost;
+  };
+  std::vector<Item> items;
+  std::vector<std::array<int32_t, 6>> merges;
+  int64_t next_slot = 0;
+  std::vector<std::pair<int32_t, int32_t>> chunks;
+  for (const Unit& u : units) {
+    chunks.clear();
+    for (int64_t k = u.lo / Lc; k <= (int64_t(u.hi) - 1) / Lc; ++k)
+      chunks.emplace_back(int32_t(std::max<int64_t>(u.lo, k * Lc)), int32_t(std::min<int64_t>(u.hi, (k + 1) * Lc)));
+    if (u.sink_hi > 0) chunks.emplace_back(0, u.sink_hi);
+    const bool split = chunks.size() >= 2;
+    const int64_t first = next_slot;
+    if (split) {
+      next_slot += int64_t(chunks.size());
+      if (next_slot > p.max_slots) return fail(PLAN_CAPACITY, "more partial-state slots than max_slots");
+      merges.push_back({u.r, u.h, u.row_lo, u.row_hi, int32_t(first), int32_t(chunks.size())});
+    }
+    for (size_t c = 0; c < chunks.size(); ++c) {
+      Item it;
+      it.r = u.r;
+      it.h = u.h;
+      it.row_lo = u.row_lo;
+      it.row_hi = u.row_hi;
+      it.kv_lo = chunks[c].first;
+      it.kv_hi = chunks[c].second;
+      it.slot = split ? int32_t(first + int64_t(c)) : -1;
+      it.cost = int64_t(it.kv_hi - it.kv_lo) + p.item_overhead;
+      items.push_back(it);
+    }
+  }
+  if (int64_t(merges.size()) > p.max_merge) return fail(PLAN_CAPACITY, "more merge entries than max_merge");
+  if (int64_t(items.size()) > int64_t(W) * p.max_items_per_worker)
+    return fail(PLAN_CAPACITY, "more items than num_workers * max_items_per_worker");
+
+  // 6. LPT assignment
+  std::vector<int32_t> order(items.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = int32_t(i);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    if (items[a].cost != items[b].cost) return items[a].cost > items[b].cost;
+    return a < b;
+  });
+  using Slot = std::pair<int64_t, int32_t>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int32_t w = 0; w < W; ++w) heap.push({0, w});
+  std::vector<std::vector<int32_t>> lists(W);
+  std::vector<int64_t> load(W, 0);
+  for (int32_t id : order) {
+    Slot s = heap.top();
+    heap.pop();
+    lists[s.second].push_back(id);
+    load[s.second] = s.first + items[id].cost;
+    heap.push({load[s.second], s.second});
+  }
+  int32_t max_on_worker = 0;
+  for (const auto& l : lists) max_on_worker = std::max<int32_t>(max_on_worker, int32_t(l.size()));
+  if (max_on_worker > p.max_items_per_worker)
+    return fail(PLAN_CAPACITY, "more items on one worker than max_items_per_worker");
+
+  // 7. serialise
+  const Layout L = layout_for(W, int64_t(items.size()), int64_t(merges.size()), batch);
+  std::memset(buf, 0, size_t(L.total_words) * sizeof(int32_t));
+  buf[HDR_NUM_ITEMS] = int32_t(items.size());
+  buf[HDR_NUM_MERGE] = int32_t(merges.size());
+  buf[HDR_NUM_SLOTS] = int32_t(next_slot);
+  buf[HDR_NUM_WORKERS] = W;
+  buf[HDR_BATCH] = batch;
+  buf[HDR_CHUNK] = int32_t(Lc);
+  buf[HDR_TILE_Q] = p.tile_q;
+  buf[HDR_OFF_ITEMS] = int32_t(L.off_items);
+  buf[HDR_OFF_MERGE] = int32_t(L.off_merge);
+  buf[HDR_OFF_QO] = int32_t(L.off_qo);
+  buf[HDR_OFF_KVLEN] = int32_t(L.off_kvlen);
+  buf[HDR_OFF_KVIND] = int32_t(L.off_kvind);
+  buf[HDR_MAX_KV_LEN] = max_kv;
+  buf[HDR_MAX_QO_LEN] = max_qo;
+  int32_t* wptr = buf + HDR_WORDS;
+  int32_t* out = buf + L.off_items;
+  int32_t pos = 0;
+  for (int32_t w = 0; w < W; ++w) {
+    wptr[w] = pos;
+    for (int32_t id : lists[w]) {
+      const Item& it = items[id];
+      int32_t* rec = out + int64_t(pos) * ITEM_WORDS;
+      rec[IT_R] = it.r;
+      rec[IT_H] = it.h;
+      rec[IT_ROW_LO] = it.row_lo;
+      rec[IT_ROW_HI] = it.row_hi;
+      rec[IT_KV_LO] = it.kv_lo;
+      rec[IT_KV_HI] = it.kv_hi;
+      rec[IT_SLOT] = it.slot;
+      rec[IT_ID] = id;
+      ++pos;
+    }
+  }
+  wptr[W] = pos;
+  for (size_t m = 0; m < merges.size(); ++m) {
+    int32_t* rec = buf + L.off_merge + int64_t(m) * MERGE_WORDS;
+    for (int k = 0; k < 6; ++k) rec[k] = merges[m][k];
+  }
+  for (int32_t r = 0; r <= batch; ++r) buf[L.off_qo + r] = batch ? qo_indptr[r] : 0;
+  for (int32_t r = 0; r < batch; ++r) buf[L.off_kvlen + r] = kv_len[r];
+  for (int32_t r = 0; r <= batch; ++r) buf[L.off_kvind + r] = batch ? kv_indptr[r] : 0;
+
+  if (stats) {
+    stats->num_items = int32_t(items.size());
+    stats->num_slots = int32_t(next_slot);
+    stats->num_merge = int32_t(merges.size());
+    stats->chunk = int32_t(Lc);
+    stats->max_kv_len = max_kv;
+    stats->max_qo_len = max_qo;
+    stats->max_items_on_worker = max_on_worker;
+    int64_t tc = 0, ml = 0;
+    for (const Item& it : items) tc += it.cost;
+    for (int64_t l : load) ml = std::max(ml, l);
+    stats->total_cost = tc;
+    stats->max_load = ml;
+    stats->used_bytes = L.total_words * int64_t(sizeof(int32_t));
+  }
+  return PLAN_OK;
+}
+
+}  // namespace bsk

@@ -1,0 +1,278 @@
+/*
+ * bsk.h -- C ABI of libbsk: batched attention over a paged, block-sparse KV
+ * cache for variable-length LLM serving, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [FI-paper]   "FLASHINFER: EFFICIENT AND CUSTOMIZABLE ATTENTION ENGINE FOR LLM
+ *                INFERENCE SERVING" (blog summary of the FlashInfer paper):
+ *                "Research methodology" 1 (block-sparse KV, composable formats),
+ *                3 (dynamic load-balanced scheduling: CPU plan, cached on the GPU,
+ *                fixed graph-compatible launch); "Results" (fused RoPE kernel,
+ *                Streaming-LLM, parallel generation).
+ *   [FI-0.6]     "FlashInfer 0.6: JIT compilation, MLA, MoE EP, Blackwell" (wiki):
+ *                "Architecture" 1 (block-sparse KV format; page indices prefetched
+ *                into on-chip shared memory), "Kernel types" (Decode: query length
+ *                1, HBM-bound, GQA; Prefill: compute-bound, chunked prefill; the
+ *                Blackwell GQA decode with sliding-window and attention-sink
+ *                masking; split-KV).
+ *   [FI-PR5329]  "FlashInfer BatchAttention: K/V stride optimisation" (analysis
+ *                of PR #5329): "Code analysis" 1 (persistent kernel over two
+ *                query-tile classes, 128 and 16 rows, grid from plan_info,
+ *                K/V stride comparison, cudaError_t status) and 2 (plan()/run()
+ *                with float and int workspace buffers, q, kv cache, out, lse).
+ *
+ * Conventions
+ *   - All memory is owned by the caller.  The library allocates no device
+ *     memory and keeps no state except a thread-local error message.
+ *   - Device pointers are HIP device addresses; `stream` is a hipStream_t
+ *     passed as void* (NULL = the default stream).  Work is enqueued
+ *     asynchronously on `stream`; errors found on the host are reported
+ *     before anything is enqueued.
+ *   - Element strides are in elements (not bytes); the last (head_dim)
+ *     dimension of every tensor must be contiguous.
+ *   - Every entry point returns a bsk_status; on failure bsk_last_error()
+ *     describes it.  No C++ exception crosses this boundary.
+ *   - run/merge launches have fixed grids and read all per-step data from
+ *     the int workspace, so they can be captured once in a hipGraph and
+ *     replayed after each new bsk_plan into the same workspace.
+ */
+#ifndef BSK_H
+#define BSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bsk_status;
+#define BSK_OK 0
+#define BSK_ERR_INVALID_ARG (-1) /* bad argument or inconsistent inputs          */
+#define BSK_ERR_UNSUPPORTED (-2) /* valid but not built (head_dim, dtype, ...)    */
+#define BSK_ERR_CAPACITY (-3)    /* plan exceeds items/slots/merge capacities     */
+#define BSK_ERR_WORKSPACE (-4)   /* a workspace is too small                      */
+#define BSK_ERR_HIP (-5)         /* a HIP runtime call failed                     */
+
+#define BSK_DTYPE_F32 0
+#define BSK_DTYPE_BF16 1
+
+#define BSK_KV_PAGED 0 /* pools [num_pages, ...], page table per request        */
+#define BSK_KV_DENSE 1 /* one contiguous [N, Hk, d] block, token offsets per req */
+
+#define BSK_ROPE_NONE 0
+#define BSK_ROPE_STREAMING 1 /* key position = rank in the query's visible set */
+#define BSK_ROPE_ABSOLUTE 2  /* key position = token index                     */
+
+#define BSK_TILE_DECODE 16   /* query-row tile of bsk_run_decode                 */
+#define BSK_TILE_PREFILL 128 /* query-row tile of bsk_run_prefill                */
+
+/*
+ * Problem description shared by plan, run and merge.  Query rows of a
+ * request are its (token i, group member u) pairs flattened as
+ * row = i * g + u with g = num_qo_heads / num_kv_heads; q head h*g + u
+ * reads kv head h.  The qo_len queries of a request are the last qo_len
+ * tokens of its KV sequence (their K/V already appended), so query i sits
+ * at position kv_len - qo_len + i, which the causal mask and the sliding
+ * window are aligned to.
+ */
+typedef struct bsk_problem {
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* 64 or 128                                          */
+  int32_t dtype;         /* q, k, v element type: BSK_DTYPE_F32 or _BF16       */
+  int32_t out_dtype;     /* out element type: BSK_DTYPE_F32 or _BF16 (lse f32) */
+  int32_t kv_mode;       /* BSK_KV_PAGED or BSK_KV_DENSE                       */
+  int32_t page_size;     /* power of two, PAGED only (ignored for DENSE)       */
+  int32_t causal;        /* 0/1: key j visible only if j <= query position     */
+  int32_t window;        /* > 0: key j visible only if qpos - j < window ...   */
+  int32_t sink;          /* ... or j < sink (attention sinks); window <= 0: off */
+  int32_t rope_mode;     /* BSK_ROPE_*; rotate-half, q and k both rotated      */
+  int32_t reserved0;
+  double rope_theta;     /* RoPE base                                          */
+  float sm_scale;        /* logit scale, e.g. 1/sqrt(head_dim)                 */
+  /* plan parameters (see bsk_plan) */
+  int32_t tile_q;        /* BSK_TILE_DECODE or BSK_TILE_PREFILL                */
+  int32_t tile_kv;       /* chunk alignment, multiple of page_size             */
+  int32_t num_workers;   /* persistent workgroups = launch grid (> 0)          */
+  int32_t split_factor;  /* target chunks per worker (>= 1)                    */
+  int32_t min_chunk;     /* lower bound of the chunk length, multiple of tile_kv */
+  int32_t max_chunk;     /* upper bound (0: kernel limit), multiple of tile_kv */
+  int32_t item_overhead; /* cost added per work item (keys)                    */
+  /* capacities (size the workspaces) */
+  int32_t max_batch;
+  int32_t max_items_per_worker;
+  int32_t max_slots;     /* partial-state slots in the float workspace         */
+  int32_t max_merge;     /* merge-table entries                                */
+} bsk_problem;
+
+/* Filled by bsk_plan; passed unchanged to run/merge. */
+typedef struct bsk_plan_info {
+  int32_t num_workers;  /* launch grid of bsk_run_*                            */
+  int32_t tile_q;
+  int32_t batch;
+  int32_t num_items;
+  int32_t num_slots;
+  int32_t num_merge;
+  int32_t chunk;        /* chunk length L_c in keys                            */
+  int32_t max_kv_len;
+  int32_t max_qo_len;
+  int32_t max_items_on_worker;
+  int64_t total_cost;   /* sum of item costs                                   */
+  int64_t max_load;     /* largest per-worker cost                             */
+  int64_t used_bytes;   /* bytes of the int workspace written                  */
+} bsk_plan_info;
+
+/*
+ * Device tensors.  PAGED: k/v are pools addressed as
+ *   k[page * k_stride_page + head * k_stride_head + slot * k_stride_tok + c]
+ * (e.g. [num_pages, Hk, page_size, d] contiguous: strides Hk*ps*d, ps*d, d);
+ * token j of request r lives in page kv_page_indices[kv_indptr[r] + j / page_size],
+ * slot j % page_size.  DENSE: token j of request r is
+ *   k[(kv_indptr[r] + j) * k_stride_tok + head * k_stride_head + c]
+ * (k_stride_page unused).  The same for v with its own strides.
+ */
+typedef struct bsk_tensors {
+  const void* q;          /* [T, Hq, d] in problem.dtype                     */
+  int64_t q_stride_tok, q_stride_head;
+  const void* k;
+  const void* v;
+  int64_t k_stride_page, k_stride_head, k_stride_tok;
+  int64_t v_stride_page, v_stride_head, v_stride_tok;
+  const int32_t* kv_page_indices; /* PAGED only                              */
+  void* out;              /* [T, Hq, d] in problem.out_dtype                 */
+  int64_t o_stride_tok, o_stride_head;
+  float* lse;             /* [T, Hq] natural-log sum-exp of scaled logits    */
+  int64_t lse_stride_tok; /* head stride is 1                                */
+  const float* rope_cos_sin; /* [rope_n_pos, d/2, 2] (cos, sin), see bsk_rope_table */
+  int32_t rope_n_pos;
+  int32_t reserved0;
+} bsk_tensors;
+
+/* Human-readable name of a status code (static string). */
+const char* bsk_status_string(bsk_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* bsk_last_error(void);
+
+/*
+ * Persistent-grid size for a kernel class on the current device: compute
+ * units times resident workgroups per CU for the tile class (tile_q 16 or
+ * 128), head_dim and dtype.  The grid must not exceed what is co-resident
+ * (a persistent launch larger than that is what [FI-PR5329, review] reports
+ * failing).  Needs a GPU.
+ */
+bsk_status bsk_device_workers(int32_t tile_q, int32_t head_dim, int32_t dtype, int32_t* num_workers);
+
+/*
+ * Workspace sizes for `problem` ([FI-PR5329, code analysis 2]: float and int
+ * workspace buffers).  int_ws: plan arrays on the device; host_ws: the same
+ * bytes on the host (pinned memory recommended), written by bsk_plan and
+ * copied in one transfer; float_ws: max_slots partial states of tile_q rows,
+ * each head_dim + 1 floats.  Pure host computation.
+ */
+bsk_status bsk_workspace_query(const bsk_problem* problem, size_t* int_ws_bytes, size_t* float_ws_bytes,
+                               size_t* host_ws_bytes);
+
+/*
+ * Build the work plan on the host and upload it ([FI-paper, methodology 3]:
+ * runtime lengths -> CPU plan that evenly spreads work over all cores ->
+ * cached on the GPU for a fixed launch).  Host inputs:
+ *   qo_indptr[batch+1]  query token offsets into q/out/lse,
+ *   kv_len[batch]       KV sequence length per request (>= qo_len),
+ *   kv_indptr[batch+1]  PAGED: offsets into kv_page_indices;
+ *                       DENSE: token offsets into k/v.
+ * Each (request, kv head, query tile) is cut into key chunks of L_c =
+ * max(min_chunk, roundup(ceil(total_cost / (num_workers * split_factor)),
+ * tile_kv)) keys at absolute multiples of L_c (plus the sink range as its own
+ * chunk), and items are assigned longest-first to the least-loaded worker.
+ * Multi-chunk units write partial states to float-workspace slots that
+ * bsk_merge_states combines.  The exact rules, tie-breaks included, are
+ * spelled out at the top of csrc/plan.cpp.
+ * host_ws receives the plan; if int_ws_dev is non-NULL its first used_bytes
+ * are then copied there with one hipMemcpyAsync on `stream` (host_ws must
+ * stay untouched until that copy completes).  int_ws_dev == NULL plans on
+ * the host only (no GPU needed).
+ * Errors: INVALID_ARG (inconsistent lengths, bad parameters), CAPACITY
+ * (more items on a worker, slots or merge entries than allowed),
+ * WORKSPACE (buffers too small), HIP.
+ */
+bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo_indptr, const int32_t* kv_len,
+                    const int32_t* kv_indptr, void* host_ws, size_t host_ws_bytes, void* int_ws_dev,
+                    size_t int_ws_bytes, void* stream, bsk_plan_info* info);
+
+/*
+ * Small-tile attention (16 query rows per item): decode ([FI-0.6, kernel
+ * types: Decode], query length 1, GQA groups of up to 16 heads) and short
+ * multi-token queries.  Persistent kernel: workgroup w runs worker w's items
+ * from the int workspace; page ids of an item are staged in LDS; K/V pages
+ * are read with coalesced 16-byte loads; logits and P.V use MFMA (bf16) or
+ * fp32 MFMA (f32 inputs); online softmax in fp32.  Single-chunk items write
+ * out/lse; multi-chunk items write partial (O, LSE) to float_ws.
+ * RoPE (bf16 only): q and every key are rotated in-kernel from the
+ * cos/sin table (K stays unrotated in the cache); STREAMING needs qo_len 1.
+ * Errors: INVALID_ARG (plan/tile mismatch, null pointers), UNSUPPORTED
+ * (head_dim, dtype, rope with f32), WORKSPACE, HIP (launch failure).
+ */
+bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                          const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
+
+/*
+ * Large-tile attention (128 query rows per item): ragged (causal) prefill,
+ * including prefill appended after cached KV ([FI-0.6, kernel types:
+ * Prefill]) and the dense shared prefix of the composable format
+ * ([FI-paper, methodology 1]).  bf16 only; QK^T and PV on bf16 MFMA with
+ * fp32 accumulation.  Same output / partial-state contract as
+ * bsk_run_decode.  Errors as bsk_run_decode (no RoPE).
+ */
+bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                           const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
+
+/*
+ * Combine the partial states of every multi-chunk unit of the plan
+ * ([FI-0.6, kernel types: split-KV]): per query row,
+ * LSE = M + ln sum_c exp(LSE_c - M) with M = max_c LSE_c, and
+ * O = sum_c exp(LSE_c - LSE) * O_c, written to t->out / t->lse.  Rows of
+ * single-chunk units are left untouched (already written by run).  Fixed
+ * grid.  Errors: INVALID_ARG, HIP.
+ */
+bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                            const void* int_ws_dev, const void* float_ws, void* stream);
+
+/*
+ * Merge two complete states row by row (the composable format's dense
+ * prefix state with a sparse suffix state, [FI-paper, methodology 1]):
+ * o_a/o_b [rows, head_dim] f32 contiguous, lse_a/lse_b [rows] f32; writes
+ * o_out [rows, head_dim] in out_dtype and lse_out [rows].  Rows whose two
+ * LSEs are both -inf get O = 0, LSE = -inf.  o_out may alias o_a or o_b
+ * only when out_dtype is F32.  Errors: INVALID_ARG, HIP.
+ */
+bsk_status bsk_merge_state_pair(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                                void* o_out, float* lse_out, int32_t rows, int32_t head_dim, int32_t out_dtype,
+                                void* stream);
+
+/*
+ * Fill the RoPE table used by the fused-RoPE decode ([FI-paper, results:
+ * fused RoPE + attention kernel]): table[p][k] = (cos, sin) of
+ * p * theta^(-2k/head_dim) for p < n_pos, k < head_dim/2, evaluated in fp64
+ * on the device and stored as f32.  table_dev: n_pos * head_dim floats.
+ * Errors: INVALID_ARG, HIP.
+ */
+bsk_status bsk_rope_table(float* table_dev, int32_t n_pos, int32_t head_dim, double theta, void* stream);
+
+/*
+ * Test hook for the block-sparse gather ([FI-0.6, architecture 1]): for
+ * every plan item, copy the item's keys [kv_lo, kv_hi) of kv head h,
+ * fetched through the same LDS-staged page-id path as the attention
+ * kernels, into k_out/v_out (problem.dtype, rows of head_dim) at row
+ * offset row_offsets[item_id] (device int64 array indexed by item id).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                            const void* int_ws_dev, const int64_t* row_offsets, void* k_out, void* v_out,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSK_H */

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: max-abs(O) <= 1e-2 and max-abs(LSE) <= 1e-3 (bf16 in, fp32
+accumulate); gather and plan-driven structure are bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_kv_plan_amd as bsk
+import oracle
+import workloads as W
+from block_sparse_kv_plan_amd.attention import BatchAttention, merge_pair, tensors_for
+from tests.gpu_util import compare, require_gpu, run, say, upload
+from tests.helpers import oracle_attention, oracle_kv
+
+pytestmark = pytest.mark.gpu
+
+
+def small(seed, kv, qo=1, Hq=8, Hk=2, d=64, ps=16, dtype=W.BF16, **kw):
+    return W.paged_batch(name=f"small-{seed}", seed=seed, kv_len=list(kv), qo_len=qo, num_qo_heads=Hq,
+                         num_kv_heads=Hk, head_dim=d, page_size=ps, dtype=dtype, **kw)
+
+
+# ------------------------------------------------------------------ gather
+
+@pytest.mark.parametrize("dtype,d", [(W.F32, 64), (W.BF16, 128)])
+def test_gather_bit_exact(dtype, d):
+    dev = require_gpu()
+    b = small(31, [17, 64, 130, 255, 1], Hq=8, Hk=2, d=d, ps=16, dtype=dtype, pool_pages=80)
+    say(f"gather {dtype} d={d}")
+    du = upload(b)
+    attn = BatchAttention.create(device=dev, num_workers=7, num_qo_heads=8, num_kv_heads=2, head_dim=d,
+                                 dtype=bsk.DTYPE_BF16 if dtype == W.BF16 else bsk.DTYPE_F32, causal=True,
+                                 max_batch=8, min_chunk=32, tile_kv=16)
+    info = attn.plan(b.qo_indptr, b.kv_len, du["kv_indptr"])
+    from tests import planbuf
+    plan = planbuf.decode(attn.host_ws.numpy())
+    items = sorted((int(x[7]), x) for lst in plan["worker_items"] for x in lst)
+    lens = np.array([int(x[5] - x[4]) for _, x in items])
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    n = int(lens.sum())
+    tdt = torch.bfloat16 if dtype == W.BF16 else torch.float32
+    ko = torch.zeros((n, d), dtype=tdt, device=dev)
+    vo = torch.zeros((n, d), dtype=tdt, device=dev)
+    out = torch.empty((5, 8, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((5, 8), dtype=torch.float32, device=dev)
+    t = tensors_for(attn.problem, du["q"], du["k"], du["v"], out, lse, page_indices=du["pages"])
+    bsk.debug_gather(attn.problem, info, t, attn.int_ws, torch.from_numpy(offs).to(dev), ko, vo,
+                     torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    kp, vp = b.physical_pools()
+    got_k, got_v = ko.float().cpu().numpy(), vo.float().cpu().numpy()
+    for (iid, x), off, ln in zip(items, offs, lens):
+        r, h, lo, hi = int(x[0]), int(x[1]), int(x[4]), int(x[5])
+        tok = np.arange(lo, hi)
+        pages = b.kv_page_indices[b.kv_page_indptr[r] + tok // 16]
+        np.testing.assert_array_equal(got_k[off:off + ln], kp[pages, h, tok % 16, :])
+        np.testing.assert_array_equal(got_v[off:off + ln], vp[pages, h, tok % 16, :])
+
+
+# ------------------------------------------------------------------ decode (16-row tiles)
+
+def test_tiny_decode_f32():
+    """4 requests, kv {17,64,130,255}, 64-page permuted pool, 8/2 heads, d 64, fp32."""
+    b = W.tiny_decode_f32()
+    O, L, attn, _ = run(b, num_workers=8, split_factor=2, min_chunk=32)
+    assert attn.info.num_merge > 0
+    compare(b, O, L, o_tol=1e-5, lse_tol=1e-5)
+
+
+def test_tiny_decode_f32_nhd_layout():
+    b = W.tiny_decode_f32()
+    O, L, _, _ = run(b, layout="NHD", num_workers=5, split_factor=3, min_chunk=16)
+    compare(b, O, L, o_tol=1e-5, lse_tol=1e-5)
+
+
+def test_llama3_decode_full():
+    """64 requests, kv lognormal [512, 8192], 32/8 heads, d 128, bf16, page 16: the benchmarked launch."""
+    b = W.llama3_decode()
+    say(f"llama3 decode: {int(b.kv_len.sum())} keys")
+    O, L, attn, _ = run(b)
+    say(f"  plan: W={attn.info.num_workers} items={attn.info.num_items} chunk={attn.info.chunk} "
+        f"merges={attn.info.num_merge}")
+    compare(b, O, L)
+
+
+def test_llama3_decode_bf16_out():
+    b = W.llama3_decode(batch=16)
+    O, L, _, _ = run(b, out_dtype=bsk.DTYPE_BF16)
+    compare(b, O, L)
+
+
+@pytest.mark.parametrize("case", [
+    dict(d=128, ps=16, Hq=32, Hk=8, kv=[1, 15, 16, 17, 300, 1000]),
+    dict(d=64, ps=1, Hq=4, Hk=4, kv=[3, 40, 77]),
+    dict(d=128, ps=8, Hq=16, Hk=1, kv=[129, 64]),
+    dict(d=128, ps=32, Hq=8, Hk=1, kv=[500, 33]),
+    dict(d=64, ps=16, Hq=32, Hk=2, kv=[90, 260]),          # g = 16
+    dict(d=128, ps=16, Hq=64, Hk=2, kv=[90, 260]),         # g = 32: a token spans two tiles
+])
+def test_decode_shapes(case):
+    kw = dict(case)
+    kv = kw.pop("kv")
+    b = small(40 + kw["ps"], kv, causal=True, **kw)
+    for W_, sf in [(3, 4), (64, 1)]:
+        O, L, _, _ = run(b, num_workers=W_, split_factor=sf, min_chunk=16)
+        compare(b, O, L)
+
+
+def test_decode_multi_token_causal_and_empty_requests():
+    kv = np.array([0, 50, 33, 7, 120])
+    qo = np.array([0, 3, 0, 7, 5])
+    b = small(50, kv, qo=qo, Hq=8, Hk=2, d=128, causal=True)
+    O, L, _, _ = run(b, num_workers=4, split_factor=2, min_chunk=16)
+    compare(b, O, L)
+
+
+def test_decode_window_sink_no_rope():
+    b = small(51, [4000, 30, 700], Hq=16, Hk=2, d=128, causal=True, window=256, sink=4, poison_invisible=True)
+    O, L, attn, _ = run(b, num_workers=16, split_factor=2, min_chunk=64)
+    compare(b, O, L)
+
+
+def test_decode_dense_kv():
+    b = W.dense_batch(name="dense-decode", seed=52, kv_len=[70, 300, 1], qo_len=[1, 1, 1], num_qo_heads=8,
+                      num_kv_heads=2, head_dim=128, dtype=W.BF16, causal=True)
+    O, L, _, _ = run(b, num_workers=6, min_chunk=32)
+    compare(b, O, L)
+
+
+def test_partial_states_match_oracle_items():
+    """Each split item's partial (O_c, LSE_c) in the float workspace against the oracle's
+    restricted attention on the item's rows and key range."""
+    b = small(53, [300, 90], Hq=8, Hk=2, d=128, causal=True)
+    O, L, attn, _ = run(b, num_workers=4, split_factor=4, min_chunk=32)
+    from tests import planbuf
+    plan = planbuf.decode(attn.host_ws.numpy())
+    fw = attn.float_ws.view(torch.float32).cpu().numpy()
+    max_slots, tq, d = attn.problem.max_slots, 16, 128
+    po = fw[:max_slots * tq * d].reshape(max_slots, tq, d)
+    pl = fw[max_slots * tq * d:max_slots * tq * (d + 1)].reshape(max_slots, tq)
+    kv = oracle_kv(b)
+    checked = 0
+    for lst in plan["worker_items"]:
+        for x in lst:
+            r, h, rlo, rhi, lo, hi, slot = (int(v) for v in x[:7])
+            if slot < 0:
+                continue
+            ro, rl = oracle.attention_partial(b.q, b.qo_indptr, b.kv_len, kv, b.num_kv_heads, b.sm_scale, r, h,
+                                              rlo, rhi, lo, hi, causal=True)
+            n = rhi - rlo
+            assert np.abs(po[slot, :n] - ro).max() <= 1e-2
+            assert np.abs(pl[slot, :n] - rl).max() <= 1e-3
+            checked += 1
+    assert checked > 0
+
+
+def test_determinism_and_page_permutation():
+    """Two runs are bit-identical, and so are runs on two page-pool permutations of the
+    same logical cache (the plan depends only on lengths)."""
+    b1 = small(54, [700, 45, 1300], Hq=32, Hk=8, d=128, pool_pages=200, perm_seed=1, causal=True)
+    b2 = small(54, [700, 45, 1300], Hq=32, Hk=8, d=128, pool_pages=200, perm_seed=2, causal=True)
+    O1, L1, _, _ = run(b1, num_workers=32)
+    O1b, L1b, _, _ = run(b1, num_workers=32)
+    O2, L2, _, _ = run(b2, num_workers=32)
+    assert np.array_equal(O1, O1b) and np.array_equal(L1, L1b)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    compare(b1, O1, L1)
+
+
+# ------------------------------------------------------------------ prefill (128-row tiles)
+
+def test_prefill_small_several_tiles():
+    kv = np.array([300, 129, 77, 1000])
+    qo = np.array([300, 40, 77, 130])
+    b = small(60, kv, qo=qo, Hq=8, Hk=2, d=128, causal=True)
+    for W_ in (5, 64):
+        O, L, _, _ = run(b, tile_q=bsk.TILE_PREFILL, num_workers=W_, split_factor=2, min_chunk=64)
+        compare(b, O, L)
+
+
+def test_prefill_head_dim_64_noncausal_and_window():
+    kv = np.array([257, 64])
+    b = small(61, kv, qo=np.array([100, 64]), Hq=4, Hk=4, d=64, causal=False)
+    O, L, _, _ = run(b, tile_q=bsk.TILE_PREFILL, num_workers=9, min_chunk=64)
+    compare(b, O, L)
+    b2 = small(62, kv, qo=np.array([100, 64]), Hq=8, Hk=2, d=128, causal=True, window=50, sink=3)
+    O, L, _, _ = run(b2, tile_q=bsk.TILE_PREFILL, num_workers=9, min_chunk=64)
+    compare(b2, O, L)
+
+
+def test_ragged_prefill_full_sampled():
+    """16 requests, new lengths lognormal [128, 4096] appended after [0, 2048] cached keys,
+    the benchmarked launch; checked on sampled query tokens (first, last, random)."""
+    b = W.ragged_prefill()
+    say(f"ragged prefill: {int(b.qo_indptr[-1])} query tokens")
+    O, L, attn, _ = run(b, tile_q=bsk.TILE_PREFILL)
+    rng = np.random.default_rng(0)
+    toks = set()
+    for r in range(b.batch_size):
+        a, c = int(b.qo_indptr[r]), int(b.qo_indptr[r + 1])
+        toks.update([a, c - 1, int(rng.integers(a, c))])
+    compare(b, O, L, tokens=sorted(toks))
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+
+
+# ------------------------------------------------------------------ composable (dense prefix + paged suffix)
+
+def run_composable(c, prefix_workers=None, suffix_workers=None):
+    dev = require_gpu()
+    pre, suf = c.prefix, c.suffix
+    Op, Lp, _, _ = run(pre, tile_q=bsk.TILE_PREFILL, num_workers=prefix_workers)
+    Os, Ls, _, _ = run(suf, num_workers=suffix_workers)
+    T, Hq, d = suf.q.shape
+    oa = torch.from_numpy(Op.astype(np.float32)).to(dev)
+    la = torch.from_numpy(Lp.astype(np.float32)).to(dev)
+    ob = torch.from_numpy(Os.astype(np.float32)).to(dev)
+    lb = torch.from_numpy(Ls.astype(np.float32)).to(dev)
+    oo = torch.empty_like(oa)
+    lo = torch.empty_like(la)
+    merge_pair(oa, la, ob, lb, oo, lo)
+    torch.cuda.synchronize()
+    return oo.double().cpu().numpy(), lo.double().cpu().numpy()
+
+
+def test_shared_prefix_composable_full():
+    """16384-token dense prefix + 64 paged suffixes [128, 1024], merged by LSE."""
+    c = W.shared_prefix()
+    O, L = run_composable(c)
+    pre, suf = c.prefix, c.suffix
+    from oracle.attention import DenseKV
+    kp, vp = suf.physical_pools()
+    ref = oracle.composable(suf.q, DenseKV(pre.dense_k, pre.dense_v, pre.kv_indptr), 16384,
+                            oracle_kv(suf, physical=True), suf.kv_len, suf.num_kv_heads, suf.sm_scale)
+    compare(suf, O, L, ref=ref)
+
+
+# ------------------------------------------------------------------ fused RoPE + window + sinks
+
+def test_streaming_rope_full():
+    """batch 8, kv uniform [32768, 131072], 64/8 heads, window 4096 + 4 sinks, RoPE theta 5e5."""
+    b = W.streaming_rope_decode()
+    say(f"streaming rope: kv {b.kv_len.tolist()}")
+    O, L, _, _ = run(b)
+    compare(b, O, L)
+
+
+@pytest.mark.parametrize("mode", ["streaming", "absolute"])
+def test_rope_small(mode):
+    b = small(70, [5000, 40, 4101, 4099], Hq=16, Hk=2, d=128, causal=True, window=4096, sink=4, rope=mode,
+              rope_theta=500000.0, poison_invisible=True)
+    O, L, _, _ = run(b, num_workers=24)
+    compare(b, O, L)
+
+
+def test_rope_head_dim_64():
+    b = small(71, [900, 20], Hq=8, Hk=1, d=64, causal=True, window=128, sink=2, rope="streaming",
+              rope_theta=10000.0, poison_invisible=True)
+    O, L, _, _ = run(b, num_workers=6)
+    compare(b, O, L)
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_capture_replan_replay():
+    """run + merge captured once in a graph; new plans (different lengths) uploaded into the
+    same workspace; each replay matches the oracle, with eager work between replays."""
+    dev = require_gpu()
+    b = small(80, [900, 2000, 33, 512], Hq=32, Hk=8, d=128, causal=True, pool_pages=400)
+    du = upload(b)
+    attn = BatchAttention.create(device=dev, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                                 dtype=bsk.DTYPE_BF16, causal=True, max_batch=4)
+    out = torch.zeros((4, 32, 128), dtype=torch.float32, device=dev)
+    lse = torch.zeros((4, 32), dtype=torch.float32, device=dev)
+    t = tensors_for(attn.problem, du["q"], du["k"], du["v"], out, lse, page_indices=du["pages"])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        attn.plan(b.qo_indptr, b.kv_len, du["kv_indptr"], stream=s)
+        attn.run(t, stream=s)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        attn.run(t, stream=s)
+    for trial, lens in enumerate([[900, 2000, 33, 512], [17, 1500, 33, 2], [640, 640, 640, 640]]):
+        kv = np.minimum(np.asarray(lens), b.kv_len)
+        attn.plan(b.qo_indptr, kv, du["kv_indptr"], stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        bt = small(80, [900, 2000, 33, 512], Hq=32, Hk=8, d=128, causal=True, pool_pages=400)
+        bt.kv_len = kv.astype(np.int32)
+        compare(bt, out.double().cpu().numpy(), lse.double().cpu().numpy())
+        _ = (out * 2).sum().item()  # eager work between replays

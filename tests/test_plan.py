@@ -1,0 +1,165 @@
+"""The C++ planner (through the C ABI, host only) must reproduce the oracle's
+reference plan bit for bit: same chunk length, same items in the same order on
+every worker, same slots and merge table."""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import block_sparse_kv_plan_amd as bsk
+import oracle
+import workloads as W
+from block_sparse_kv_plan_amd.attention import make_problem
+from tests import planbuf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def cpp_plan(problem, qo_len, kv_len, kv_indptr=None):
+    qo_len = np.asarray(qo_len, dtype=np.int64)
+    kv_len = np.asarray(kv_len, dtype=np.int64)
+    qo_indptr = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int32)
+    if kv_indptr is None:
+        kv_indptr = np.concatenate([[0], np.cumsum((kv_len + 15) // 16)]).astype(np.int32)
+    _, _, host_b = bsk.workspace_query(problem)
+    host = np.zeros(host_b, dtype=np.uint8)
+    info = bsk.plan(problem, qo_indptr, kv_len.astype(np.int32), kv_indptr, host)
+    return info, planbuf.decode(host), (qo_indptr, kv_indptr)
+
+
+KERNEL_MAX_PAGES = 1024  # page ids one item may stage in LDS (documented cap behind max_chunk = 0)
+
+
+def effective_max_chunk(problem):
+    if problem.max_chunk > 0 or problem.kv_mode == bsk.KV_DENSE:
+        return problem.max_chunk
+    return (KERNEL_MAX_PAGES * problem.page_size) // problem.tile_kv * problem.tile_kv
+
+
+def ref_params(problem):
+    return oracle.PlanParams(
+        num_qo_heads=problem.num_qo_heads, num_kv_heads=problem.num_kv_heads, tile_q=problem.tile_q,
+        tile_kv=problem.tile_kv, num_workers=problem.num_workers, split_factor=problem.split_factor,
+        min_chunk=problem.min_chunk, max_chunk=effective_max_chunk(problem), item_overhead=problem.item_overhead,
+        max_items_per_worker=problem.max_items_per_worker, max_slots=problem.max_slots,
+        max_merge=problem.max_merge, causal=bool(problem.causal), window=max(problem.window, 0),
+        sink=problem.sink if problem.window > 0 else 0)
+
+
+def assert_same_plan(problem, qo_len, kv_len):
+    info, got, (qo_indptr, kv_indptr) = cpp_plan(problem, qo_len, kv_len)
+    ref = oracle.plan_ref(qo_len, kv_len, ref_params(problem))
+    assert got["chunk"] == ref["chunk"] == info.chunk
+    assert got["num_items"] == len(ref["items"]) == info.num_items
+    assert got["num_slots"] == ref["num_slots"] == info.num_slots
+    assert got["num_merge"] == len(ref["merge"]) == info.num_merge
+    for w in range(problem.num_workers):
+        ids = ref["worker_items"][w]
+        want = np.concatenate([ref["items"][ids], np.asarray(ids, dtype=np.int64)[:, None]], axis=1) \
+            if ids else np.zeros((0, 8), dtype=np.int64)
+        assert np.array_equal(got["worker_items"][w].astype(np.int64), want), f"worker {w}"
+    assert np.array_equal(got["merge"][:, :6].astype(np.int64), ref["merge"])
+    assert info.max_load == int(ref["load"].max()) if len(ref["items"]) else True
+    assert np.array_equal(got["qo_indptr"], qo_indptr)
+    assert np.array_equal(got["kv_len"], np.asarray(kv_len, dtype=np.int32))
+    assert np.array_equal(got["kv_indptr"], kv_indptr)
+    return info, ref
+
+
+def decode_problem(Hq, Hk, d, W_, dtype=bsk.DTYPE_BF16, **kw):
+    return make_problem(num_qo_heads=Hq, num_kv_heads=Hk, head_dim=d, dtype=dtype, num_workers=W_,
+                        max_batch=kw.pop("max_batch", 256), **kw)
+
+
+def test_tiny_decode_matches_golden_and_oracle():
+    p = decode_problem(8, 2, 64, 8, dtype=bsk.DTYPE_F32, causal=True, split_factor=2, min_chunk=32,
+                       max_chunk=1024, max_items_per_worker=16, max_slots=64, max_merge=64)
+    info, ref = assert_same_plan(p, [1, 1, 1, 1], [17, 64, 130, 255])
+    assert info.chunk == 64
+    assert ref["worker_items"] == [[2, 12], [3, 14], [4, 15], [5, 16], [7, 13], [8, 17], [10, 0, 6], [11, 1, 9]]
+
+
+def test_llama3_decode_plan():
+    qo, kv = W.llama3_decode_lengths()
+    p = decode_problem(32, 8, 128, 768, causal=True, max_chunk=4096)
+    info, _ = assert_same_plan(p, qo, kv)
+    assert info.num_merge > 0
+
+
+def test_ragged_prefill_plan():
+    qo, kv = W.ragged_prefill_lengths()
+    p = decode_problem(32, 8, 128, 512, causal=True, tile_q=bsk.TILE_PREFILL, max_chunk=8192)
+    assert_same_plan(p, qo, kv)
+
+
+def test_shared_prefix_plans():
+    s = W.shared_prefix_lengths()
+    pre = make_problem(num_qo_heads=32, num_kv_heads=8, head_dim=128, dtype=bsk.DTYPE_BF16, kv_mode=bsk.KV_DENSE,
+                       tile_q=bsk.TILE_PREFILL, num_workers=512, max_batch=1, max_chunk=4096)
+    info, _, _ = cpp_plan(pre, [64], [16384], np.array([0, 16384], dtype=np.int32))
+    ref = oracle.plan_ref([64], [16384], ref_params(pre))
+    assert info.chunk == ref["chunk"] and info.num_items == len(ref["items"])
+    suf = decode_problem(32, 8, 128, 768, causal=True, max_chunk=4096)
+    assert_same_plan(suf, np.ones(len(s), dtype=np.int64), s)
+
+
+def test_streaming_window_plan():
+    qo, kv = W.streaming_rope_decode_lengths()
+    p = decode_problem(64, 8, 128, 768, causal=True, window=4096, sink=4, max_chunk=4096)
+    info, ref = assert_same_plan(p, qo, kv)
+    # every unit ends with its sink chunk [0, 4)
+    assert all((it[4], it[5]) == (0, 4) for it in ref["items"] if it[5] <= 4)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_plans(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 20))
+    kv = rng.integers(0, 3000, size=B)
+    qo = np.minimum(kv, rng.choice([0, 1, 1, 3, 17, 200], size=B))
+    Hk = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    tile_q = int(rng.choice([bsk.TILE_DECODE, bsk.TILE_PREFILL]))
+    window = int(rng.choice([0, 0, 5, 64, 1000]))
+    tile_kv = int(rng.choice([16, 32, 64]))
+    p = decode_problem(Hk * g, Hk, 64, int(rng.integers(1, 70)), tile_q=tile_q, causal=bool(rng.integers(0, 2)),
+                       window=window, sink=int(rng.integers(0, 9)), tile_kv=tile_kv,
+                       split_factor=int(rng.integers(1, 5)), min_chunk=tile_kv * int(rng.integers(1, 5)),
+                       max_chunk=tile_kv * int(rng.choice([0, 16, 64])) or 0, item_overhead=int(rng.integers(0, 40)),
+                       max_items_per_worker=4096, max_slots=1 << 20, max_merge=1 << 20)
+    if p.max_chunk and p.max_chunk < p.min_chunk:
+        p.max_chunk = p.min_chunk
+    assert_same_plan(p, qo, kv)
+
+
+def test_capacity_and_invalid_errors():
+    p = decode_problem(8, 2, 64, 2, max_items_per_worker=4, max_chunk=1024)
+    with pytest.raises(bsk.BskError) as e:
+        cpp_plan(p, [1] * 40, [100] * 40)
+    assert e.value.status == bsk.ERR_CAPACITY
+    with pytest.raises(bsk.BskError) as e:
+        cpp_plan(p, [5], [3])
+    assert e.value.status == bsk.ERR_INVALID_ARG
+    p2 = decode_problem(8, 2, 64, 2, max_chunk=1 << 20)
+    with pytest.raises(bsk.BskError) as e:
+        bsk.workspace_query(p2)
+    assert e.value.status == bsk.ERR_INVALID_ARG  # page list would overflow LDS
+    p3 = decode_problem(8, 2, 96, 2)
+    with pytest.raises(bsk.BskError) as e:
+        bsk.workspace_query(p3)
+    assert e.value.status == bsk.ERR_UNSUPPORTED
+
+
+def test_planner_under_host_sanitizers():
+    """plan.cpp built with g++ and AddressSanitizer/UBSan, driven over random inputs."""
+    drv = os.path.join(ROOT, "tests", "plan_fuzz.cpp")
+    src = os.path.join(ROOT, "block_sparse_kv_plan_amd", "csrc", "plan.cpp")
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "fuzz")
+        subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                               "-fno-sanitize-recover=all", "-I", os.path.dirname(src), drv, src, "-o", exe])
+        out = subprocess.run([exe, "300"], capture_output=True, text=True, timeout=300)
+        assert out.returncode == 0, out.stdout + out.stderr
+        assert "ok" in out.stdout

@@ -284,31 +284,48 @@ def tiny_decode_f32(seed: int = 1, perm_seed=None) -> Batch:
                        pool_pages=64, sm_scale=1.0 / 8.0, perm_seed=perm_seed)
 
 
+def llama3_decode_lengths(seed: int = 2, batch: int = 64, lo: int = 512, hi: int = 8192):
+    kv = lognormal_lengths(rng_for(seed, LEN_STREAM), batch, lo, hi)
+    return np.ones(batch, dtype=np.int64), kv
+
+
 def llama3_decode(seed: int = 2, batch: int = 64, lo: int = 512, hi: int = 8192, perm_seed=None) -> Batch:
     """Llama-3-8B-shaped decode layer: 32 q / 8 kv heads, d 128, bf16, page_size 16,
     kv lengths lognormal clipped to [lo, hi]."""
-    kv = lognormal_lengths(rng_for(seed, LEN_STREAM), batch, lo, hi)
+    _, kv = llama3_decode_lengths(seed, batch, lo, hi)
     return paged_batch(name="llama3_8b_paged_decode_bf16", seed=seed, kv_len=kv, qo_len=1,
                        num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=BF16,
                        perm_seed=perm_seed)
+
+
+def ragged_prefill_lengths(seed: int = 3, batch: int = 16, q_lo: int = 128, q_hi: int = 4096,
+                           p_lo: int = 0, p_hi: int = 2048):
+    r = rng_for(seed, LEN_STREAM)
+    qlen = lognormal_lengths(r, batch, q_lo, q_hi)
+    plen = uniform_lengths(r, batch, p_lo, p_hi)
+    return qlen, plen + qlen
 
 
 def ragged_prefill(seed: int = 3, batch: int = 16, q_lo: int = 128, q_hi: int = 4096,
                    p_lo: int = 0, p_hi: int = 2048) -> Batch:
     """Ragged causal prefill appended after cached KV: new lengths lognormal [q_lo, q_hi],
     existing prefix uniform [p_lo, p_hi]; 32 q / 8 kv heads, d 128, bf16, page_size 16."""
-    r = rng_for(seed, LEN_STREAM)
-    qlen = lognormal_lengths(r, batch, q_lo, q_hi)
-    plen = uniform_lengths(r, batch, p_lo, p_hi)
+    qlen, kvlen = ragged_prefill_lengths(seed, batch, q_lo, q_hi, p_lo, p_hi)
+    plen = kvlen - qlen
     return paged_batch(name="ragged_causal_prefill_append_bf16", seed=seed, kv_len=plen + qlen, qo_len=qlen,
                        num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=BF16, causal=True)
+
+
+def shared_prefix_lengths(seed: int = 4, branches: int = 64, s_lo: int = 128, s_hi: int = 1024):
+    """Suffix lengths of the branches."""
+    return uniform_lengths(rng_for(seed, LEN_STREAM), branches, s_lo, s_hi)
 
 
 def shared_prefix(seed: int = 4, branches: int = 64, prefix_len: int = 16384,
                   s_lo: int = 128, s_hi: int = 1024) -> Composable:
     """Shared 16384-token dense prefix + 64 paged branch suffixes uniform [128, 1024],
     one decode token per branch; 32 q / 8 kv heads, d 128, bf16, page_size 16."""
-    slen = uniform_lengths(rng_for(seed, LEN_STREAM), branches, s_lo, s_hi)
+    slen = shared_prefix_lengths(seed, branches, s_lo, s_hi)
     suffix = paged_batch(name="shared_prefix_suffix_bf16", seed=seed, kv_len=slen, qo_len=1,
                          num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=BF16,
                          causal=True)
@@ -317,11 +334,16 @@ def shared_prefix(seed: int = 4, branches: int = 64, prefix_len: int = 16384,
     return Composable(prefix=prefix, suffix=suffix)
 
 
+def streaming_rope_decode_lengths(seed: int = 5, batch: int = 8, lo: int = 32768, hi: int = 131072):
+    kv = uniform_lengths(rng_for(seed, LEN_STREAM), batch, lo, hi)
+    return np.ones(batch, dtype=np.int64), kv
+
+
 def streaming_rope_decode(seed: int = 5, batch: int = 8, lo: int = 32768, hi: int = 131072,
                           window: int = 4096, sink: int = 4, rope: str = "streaming") -> Batch:
     """Long-context Streaming-LLM decode: kv uniform [lo, hi], 64 q / 8 kv heads, d 128, bf16,
     page_size 16, K cached unrotated, RoPE theta 5e5 applied in-kernel, window 4096 + 4 sinks."""
-    kv = uniform_lengths(rng_for(seed, LEN_STREAM), batch, lo, hi)
+    _, kv = streaming_rope_decode_lengths(seed, batch, lo, hi)
     return paged_batch(name="streaming_rope_window_sink_decode_bf16", seed=seed, kv_len=kv, qo_len=1,
                        num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=16, dtype=BF16,
                        causal=True, window=window, sink=sink, rope=rope, rope_theta=500000.0,
