@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged / block-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline: paged GQA decode of a Llama-3-8B-shaped layer (batch 64, 32 q / 8
+kv heads, head_dim 128, bf16, page 16, kv lengths lognormal in [512, 8192]).
+One step = host plan + plan upload + decode kernel + state merge, i.e. the
+whole hot path for one batch; two workspaces alternate so the host plan of
+step i+1 overlaps the GPU work of step i.  The KV cache is rotated over
+four device copies so no step reads what the previous one left in the
+256 MB Infinity Cache.  ``value`` is algorithmic bytes (visible K/V + q +
+out + lse + page ids) per wall-clock step, in TB/s.
+
+Also reported (same JSON line): the decode kernel's roofline (HIP events on
+its own stream), the fp64 oracle timed on a bounded sample of the same
+batch on the host cores, and secondary measurements of the ragged causal
+prefill (TFLOP/s vs bf16 MFMA peak), the shared-prefix composable format
+and the fused-RoPE streaming decode.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device.h", "args.h", "layout.h"):
+        with open(os.path.join(ROOT, "block_sparse_kv_plan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(batch, out_bytes=4):
+    """Algorithmic HBM bytes of one decode pass: each visible key's K and V rows of every kv
+    head, q, out, lse and the page ids read."""
+    import numpy as np
+    kv = batch.kv_len.astype(np.int64)
+    if batch.window > 0:
+        vis = np.minimum(kv, batch.window + batch.sink)
+    else:
+        vis = kv
+    el = 2 if batch.dtype == "bf16" else 4
+    T = int(batch.qo_indptr[-1])
+    kvb = int(vis.sum()) * batch.num_kv_heads * batch.head_dim * 2 * el
+    qb = T * batch.num_qo_heads * batch.head_dim * el
+    ob = T * batch.num_qo_heads * (batch.head_dim * out_bytes + 4)
+    pages = int(((vis + batch.page_size - 1) // batch.page_size).sum()) * 4
+    return kvb + qb + ob + pages
+
+
+def prefill_flops(batch):
+    """4 d Hq flops per unmasked (query, key) pair of a causal, bottom-right aligned prefill."""
+    import numpy as np
+    Q = batch.qo_len.astype(np.int64)
+    P = batch.kv_len.astype(np.int64) - Q
+    pairs = int((Q * P + Q * (Q + 1) // 2).sum())
+    return 4 * batch.head_dim * batch.num_qo_heads * pairs, pairs
+
+
+def make_attention(batch, tile_q, out_dtype, device, **kw):
+    import block_sparse_kv_plan_amd as bsk
+    from block_sparse_kv_plan_amd.attention import BatchAttention
+    rope_mode = {"none": bsk.ROPE_NONE, "streaming": bsk.ROPE_STREAMING, "absolute": bsk.ROPE_ABSOLUTE}[batch.rope]
+    return BatchAttention.create(
+        device=device, num_qo_heads=batch.num_qo_heads, num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim,
+        dtype=bsk.DTYPE_BF16 if batch.dtype == "bf16" else bsk.DTYPE_F32, out_dtype=out_dtype,
+        kv_mode=bsk.KV_DENSE if batch.kv_mode == "dense" else bsk.KV_PAGED,
+        page_size=batch.page_size if batch.kv_mode == "paged" else 16, causal=batch.causal, window=batch.window,
+        sink=batch.sink, rope_mode=rope_mode, rope_theta=batch.rope_theta, sm_scale=batch.sm_scale,
+        tile_q=tile_q, max_batch=max(1, batch.batch_size), **kw)
+
+
+class Runner:
+    """Device copies of one batch plus two alternating plan workspaces."""
+
+    def __init__(self, batch, tile_q, copies, device, out_dtype=0):
+        import torch
+
+        import block_sparse_kv_plan_amd as bsk
+        from block_sparse_kv_plan_amd.attention import tensors_for
+        from tests.gpu_util import rope_positions_needed, upload
+        self.batch = batch
+        self.attn = [make_attention(batch, tile_q, out_dtype, device) for _ in range(2)]
+        T = int(batch.qo_indptr[-1])
+        o_dt = torch.bfloat16 if out_dtype == bsk.DTYPE_BF16 else torch.float32
+        self.out = torch.zeros((T, batch.num_qo_heads, batch.head_dim), dtype=o_dt, device=device)
+        self.lse = torch.zeros((T, batch.num_qo_heads), dtype=torch.float32, device=device)
+        self.rope = None
+        if batch.rope != "none":
+            n_pos = rope_positions_needed(batch)
+            self.rope = torch.empty((n_pos, batch.head_dim // 2, 2), dtype=torch.float32, device=device)
+            bsk.rope_table(self.rope, n_pos, batch.head_dim, batch.rope_theta, torch.cuda.current_stream())
+        self.dev = []
+        first = upload(batch, device=device)
+        self.kv_indptr = first["kv_indptr"]
+        self.dev.append(first)
+        for _ in range(copies - 1):
+            self.dev.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in first.items()})
+        self.tensors = [tensors_for(self.attn[0].problem, d["q"], d["k"], d["v"], self.out, self.lse,
+                                    page_indices=d["pages"], rope=self.rope) for d in self.dev]
+
+    def step(self, i, stream, ev=None, copy_stream=None):
+        """One pass of the hot path: host plan + upload (on the copy stream when given),
+        the attention kernel, then the split-KV state merge."""
+        import block_sparse_kv_plan_amd as bsk
+        a = self.attn[i % 2]
+        a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, copy_stream=copy_stream)
+        t = self.tensors[i % len(self.tensors)]
+        if copy_stream is not None:
+            stream.wait_event(a._uploaded)
+        if ev is not None:
+            ev[0].record(stream)
+        a.run(t, stream=stream, merge=False)
+        if ev is not None:
+            ev[1].record(stream)
+        if not a.problem.fused_merge:
+            bsk.merge_states(a.problem, a.info, t, a.int_ws, a.float_ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+
+def timed(runner, steps, warmup):
+    """Wall time per step over `steps` back-to-back steps, and the attention kernel's and the
+    merge's mean durations from events on their launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    copy_stream = None  # a separate upload queue measured slower (cross-queue waits) than in-stream copies
+    for i in range(warmup):
+        runner.step(i, stream, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        runner.step(warmup + i, stream, evs[i], copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    kern = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
+    merge = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
+    kern.sort()
+    return {"wall_s": wall, "kernel_s_mean": sum(kern) / len(kern), "kernel_s_median": kern[len(kern) // 2],
+            "kernel_s_min": kern[0], "merge_s_mean": sum(merge) / len(merge)}
+
+
+def cpu_baseline(batch, budget_s=15.0):
+    """fp64 oracle on the host: requests one at a time until the budget is used; the rate is
+    scaled to the metric's unit (algorithmic bytes / oracle seconds)."""
+    import copy
+
+    import numpy as np
+
+    import oracle
+    from tests.helpers import oracle_kv
+    kv = oracle_kv(batch)  # host view of the cache, built once outside the timed calls
+    done, t_used, bytes_done = 0, 0.0, 0
+    for r in range(batch.batch_size):
+        sub = copy.copy(batch)
+        t0 = time.perf_counter()
+        oracle.attention(batch.q, batch.qo_indptr, batch.kv_len, kv, batch.num_kv_heads, batch.sm_scale,
+                         causal=batch.causal, window=batch.window, sink=batch.sink, rope=batch.rope,
+                         rope_theta=batch.rope_theta,
+                         tokens=list(range(int(batch.qo_indptr[r]), int(batch.qo_indptr[r + 1]))))
+        t_used += time.perf_counter() - t0
+        sub.kv_len = batch.kv_len[r:r + 1]
+        sub.qo_indptr = np.array([0, int(batch.qo_indptr[r + 1] - batch.qo_indptr[r])])
+        bytes_done += decode_bytes(sub)
+        done += 1
+        if t_used > budget_s:
+            break
+    return {"value": bytes_done / t_used / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {batch.batch_size} requests of the same batch (fp64 numpy, single-threaded "
+                      f"einsum path), {t_used:.1f} s"}
+
+
+def load_traffic(name, launches_bytes):
+    """Measured HBM bytes of the decode kernel from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="", help="profiling aid: run just this workload (decode|prefill|composable|rope)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU "
+              "path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_kv_plan_amd as bsk
+    import workloads as W
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    result = {}
+    secondary = {}
+
+    if args.only in ("", "decode"):
+        log("decode: generating the Llama-3-8B-shaped batch")
+        b = W.llama3_decode()
+        nbytes = decode_bytes(b)
+        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device)
+        log(f"decode: {int(b.kv_len.sum())} keys, {nbytes / 1e9:.3f} GB per step; timing {args.steps} steps")
+        m = timed(runner, args.steps, args.warmup)
+        info = runner.attn[0].info
+        achieved = nbytes / m["kernel_s_mean"] / 1e9
+        traffic = load_traffic("decode_llama3", nbytes)
+        result = {
+            "metric": "paged decode HBM TB/s (% of 8 TB/s peak); ragged prefill TFLOPS (% MFMA peak)",
+            "value": round(nbytes / m["wall_s"] / 1e12, 4),
+            "unit": "TB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(m["wall_s"] * 1e3, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "llama3_8b_paged_decode_bf16", "batch": 64, "num_qo_heads": 32,
+                       "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
+                       "kv_len": "lognormal clipped to [512, 8192]", "total_kv_tokens": int(b.kv_len.sum()),
+                       "out_dtype": "f32", "num_workers": info.num_workers, "items": info.num_items,
+                       "chunk": info.chunk, "merges": info.num_merge,
+                       "plan_imbalance": round(info.max_load / max(1.0, info.total_cost / info.num_workers), 3),
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic, "kernel": "decode_kernel<bf16,128,paged>",
+                         "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2),
+                         "kernel_us_median": round(m["kernel_s_median"] * 1e6, 2),
+                         "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
+                         "algorithmic_bytes_per_launch": nbytes},
+        }
+        if not args.no_cpu:
+            log("decode: timing the fp64 oracle on a bounded sample")
+            result["cpu_baseline"] = cpu_baseline(b)
+        del runner
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "prefill"):
+        log("prefill: ragged causal prefill with append")
+        b = W.ragged_prefill()
+        flops, pairs = prefill_flops(b)
+        runner = Runner(b, bsk.TILE_PREFILL, copies=1, device=device)
+        m = timed(runner, max(5, args.steps // 5), 3)
+        tf = flops / m["kernel_s_mean"] / 1e12
+        secondary["ragged_prefill"] = {
+            "workload": "ragged_causal_prefill_append_bf16: 16 requests, q lognormal [128,4096] after "
+                        "uniform [0,2048] cached keys, 32q/8kv, d128",
+            "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 1), "step_ms": round(m["wall_s"] * 1e3, 3),
+            "unmasked_pairs": pairs, "flops": flops}
+        del runner
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "rope"):
+        log("rope: long-context streaming decode with fused RoPE, window 4096 + 4 sinks")
+        b = W.streaming_rope_decode()
+        nbytes = decode_bytes(b)
+        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device)
+        m = timed(runner, args.steps, args.warmup)
+        secondary["streaming_rope_decode"] = {
+            "workload": "streaming_rope_window_sink_decode_bf16: batch 8, kv uniform [32768,131072], 64q/8kv, "
+                        "d128, window 4096 + 4 sinks, RoPE theta 5e5 in-kernel",
+            "kernel_gbs": round(nbytes / m["kernel_s_mean"] / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / m["kernel_s_mean"] / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2), "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
+            "step_us": round(m["wall_s"] * 1e6, 1), "algorithmic_bytes": nbytes}
+        del runner
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "composable"):
+        log("composable: shared 16384-token dense prefix + 64 paged suffixes")
+        c = W.shared_prefix()
+        from block_sparse_kv_plan_amd.attention import merge_pair
+        pre = Runner(c.prefix, bsk.TILE_PREFILL, copies=1, device=device)
+        suf = Runner(c.suffix, bsk.TILE_DECODE, copies=1, device=device)
+        fin_o = torch.empty_like(suf.out)
+        fin_l = torch.empty_like(suf.lse)
+        stream = torch.cuda.current_stream()
+        n = max(10, args.steps // 2)
+
+        def one(i):
+            pre.step(i, stream)
+            suf.step(i, stream)
+            merge_pair(pre.out, pre.lse, suf.out, suf.lse, fin_o, fin_l, stream)
+
+        for i in range(3):
+            one(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for i in range(n):
+            one(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n
+        gpu = e0.elapsed_time(e1) * 1e-3 / n
+        pb = 16384 * 8 * 128 * 2 * 2
+        sb = decode_bytes(c.suffix)
+        secondary["shared_prefix_composable"] = {
+            "workload": "shared_prefix_composable_bf16: 16384-token dense prefix + 64 paged suffixes uniform "
+                        "[128,1024], 32q/8kv, d128",
+            "gpu_us_per_step": round(gpu * 1e6, 1), "wall_us_per_step": round(wall * 1e6, 1),
+            "effective_gbs": round((pb + sb) / gpu / 1e9, 1), "algorithmic_bytes": pb + sb}
+        del pre, suf
+        torch.cuda.empty_cache()
+
+    if result:
+        result["secondary"] = secondary
+        result["kernel_source_hash"] = kernel_source_hash()
+        print(json.dumps(result), flush=True)
+    else:
+        print(json.dumps({"secondary": secondary}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ i32, i64, f32, f64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.
 class Problem(ctypes.Structure):
     _fields_ = [("num_qo_heads", i32), ("num_kv_heads", i32), ("head_dim", i32), ("dtype", i32),
                 ("out_dtype", i32), ("kv_mode", i32), ("page_size", i32), ("causal", i32), ("window", i32),
-                ("sink", i32), ("rope_mode", i32), ("reserved0", i32), ("rope_theta", f64), ("sm_scale", f32),
+                ("sink", i32), ("rope_mode", i32), ("fused_merge", i32), ("rope_theta", f64), ("sm_scale", f32),
                 ("tile_q", i32), ("tile_kv", i32), ("num_workers", i32), ("split_factor", i32),
                 ("min_chunk", i32), ("max_chunk", i32), ("item_overhead", i32), ("max_batch", i32),
                 ("max_items_per_worker", i32), ("max_slots", i32), ("max_merge", i32)]
@@ -59,7 +59,7 @@ _lib.bsk_status_string.argtypes = [i32]
 _lib.bsk_last_error.restype = ctypes.c_char_p
 _lib.bsk_last_error.argtypes = []
 _sig = {
-    "bsk_device_workers": [i32, i32, i32, P(i32)],
+    "bsk_device_workers": [P(Problem), P(i32)],
     "bsk_workspace_query": [P(Problem), P(ctypes.c_size_t), P(ctypes.c_size_t), P(ctypes.c_size_t)],
     "bsk_plan": [P(Problem), i32, vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, P(PlanInfo)],
     "bsk_run_decode": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
@@ -120,9 +120,9 @@ def last_error() -> str:
     return _lib.bsk_last_error().decode()
 
 
-def device_workers(tile_q: int, head_dim: int, dtype: int) -> int:
+def device_workers(problem: Problem) -> int:
     out = i32(0)
-    _ok(_lib.bsk_device_workers(tile_q, head_dim, dtype, ctypes.byref(out)))
+    _ok(_lib.bsk_device_workers(ctypes.byref(problem), ctypes.byref(out)))
     return out.value
 
 

@@ -28,7 +28,7 @@ def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE
                  page_size=16, causal=False, window=0, sink=0, rope_mode=ROPE_NONE, rope_theta=10000.0,
                  sm_scale=None, tile_q=TILE_DECODE, num_workers, tile_kv=None, split_factor=None,
                  min_chunk=None, max_chunk=0, item_overhead=0, max_batch, max_items_per_worker=None,
-                 max_slots=None, max_merge=None) -> Problem:
+                 max_slots=None, max_merge=None, fused_merge=0) -> Problem:
     d = DEFAULTS[tile_q]
     tile_kv = tile_kv if tile_kv is not None else max(d["tile_kv"], page_size if kv_mode == KV_PAGED else 1)
     kmax = max_items_per_worker if max_items_per_worker is not None else d["max_items_per_worker"]
@@ -37,6 +37,7 @@ def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE
     p.dtype, p.out_dtype, p.kv_mode, p.page_size = dtype, out_dtype, kv_mode, page_size
     p.causal, p.window, p.sink = int(causal), int(window), int(sink)
     p.rope_mode, p.rope_theta = rope_mode, float(rope_theta)
+    p.fused_merge = int(fused_merge)
     p.sm_scale = float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(head_dim))
     p.tile_q, p.tile_kv, p.num_workers = tile_q, tile_kv, num_workers
     p.split_factor = split_factor if split_factor is not None else d["split_factor"]
@@ -78,7 +79,11 @@ def tensors_for(problem: Problem, q, k, v, out, lse, page_indices=None, layout: 
 
 
 class BatchAttention:
-    """Owns the workspaces of one problem; plan() per step, run() per layer."""
+    """Owns the workspaces of one problem; plan() per step, run() per layer.
+
+    The plan upload can go on its own copy stream: it then waits (on the GPU)
+    for the previous run that read this workspace, and run() waits for the
+    upload, so a host plan plus its copy overlap the GPU work already queued."""
 
     def __init__(self, problem: Problem, device="cuda"):
         self.problem = problem
@@ -88,33 +93,44 @@ class BatchAttention:
         self.float_ws = torch.empty(max(float_b, 16), dtype=torch.uint8, device=self.device)
         self.host_ws = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
         self.info: Optional[PlanInfo] = None
-        self._upload_done = None
+        self._uploaded = torch.cuda.Event()   # the plan copy out of host_ws has completed
+        self._consumed = torch.cuda.Event()   # the last run reading int_ws has completed
+        self._upload_pending = False
+        self._upload_stream = None
+        self._ran = False
 
     @classmethod
     def create(cls, *, device="cuda", num_workers=None, **kw):
         if num_workers is None:
-            num_workers = device_workers(kw.get("tile_q", TILE_DECODE), kw["head_dim"], kw["dtype"])
+            num_workers = device_workers(make_problem(num_workers=1, **kw))
         return cls(make_problem(num_workers=num_workers, **kw), device=device)
 
-    def plan(self, qo_indptr, kv_len, kv_indptr, stream=None) -> PlanInfo:
-        if self._upload_done is not None:
-            self._upload_done.synchronize()  # the previous plan's copy still reads host_ws
+    def plan(self, qo_indptr, kv_len, kv_indptr, stream=None, copy_stream=None) -> PlanInfo:
+        if self._upload_pending:
+            self._uploaded.synchronize()  # host_ws is still being read by the previous copy
         stream = stream or torch.cuda.current_stream(self.device)
+        up = copy_stream if copy_stream is not None else stream
+        if copy_stream is not None and self._ran:
+            up.wait_event(self._consumed)  # do not overwrite int_ws under a running kernel
         self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
-                         self.host_ws, self.int_ws, stream)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        self._upload_done = ev
+                         self.host_ws, self.int_ws, up)
+        self._uploaded.record(up)
+        self._upload_pending = True
+        self._upload_stream = up
         return self.info
 
     def run(self, tensors: Tensors, stream=None, merge: bool = True):
         stream = stream or torch.cuda.current_stream(self.device)
+        if self._upload_stream is not None and self._upload_stream != stream:
+            stream.wait_event(self._uploaded)
         if self.problem.tile_q == TILE_DECODE:
             run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         else:
             run_prefill(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
-        if merge:
+        if merge and not self.problem.fused_merge:
             merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        self._consumed.record(stream)
+        self._ran = True
 
 
 def merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):

@@ -28,6 +28,7 @@ struct AttnArgs {
   float* part_o;    // [slots][tile_q][D]
   float* part_lse;  // [slots][tile_q]
   const int32_t* ws;
+  int32_t* ws_rw;     // same buffer: the arrival counters are updated in place
   const float* rope;  // [n_pos][D/2][2]
   int32_t rope_n_pos;
   int32_t group;
@@ -36,7 +37,8 @@ struct AttnArgs {
   int32_t window;
   int32_t sink;
   int32_t out_bf16;
-  float scale_log2;  // sm_scale * log2(e): logits are kept in base 2
+  int32_t fused_merge;  // 1: the chunk that completes a split unit merges it in-kernel
+  float scale_log2;     // sm_scale * log2(e): logits are kept in base 2
 };
 
 struct MergeArgs {

@@ -53,6 +53,7 @@ bsk_status check_problem(const bsk_problem* p) {
   if (p->kv_mode == BSK_KV_PAGED && (!is_pow2(p->page_size) || p->page_size > 65536))
     return fail(BSK_ERR_INVALID_ARG, "page_size must be a power of two <= 65536");
   if (p->causal != 0 && p->causal != 1) return fail(BSK_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->fused_merge != 0 && p->fused_merge != 1) return fail(BSK_ERR_INVALID_ARG, "fused_merge must be 0 or 1");
   if (p->window > 0 && p->sink < 0) return fail(BSK_ERR_INVALID_ARG, "sink must be >= 0");
   if (p->rope_mode < BSK_ROPE_NONE || p->rope_mode > BSK_ROPE_ABSOLUTE) return fail(BSK_ERR_INVALID_ARG, "rope_mode");
   if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
@@ -159,6 +160,8 @@ bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* 
   a.part_o = fw;
   a.part_lse = fw ? fw + size_t(p.max_slots) * p.tile_q * p.head_dim : nullptr;
   a.ws = static_cast<const int32_t*>(int_ws);
+  a.ws_rw = static_cast<int32_t*>(const_cast<void*>(int_ws));
+  a.fused_merge = p.fused_merge != 0;
   a.rope = t.rope_cos_sin;
   a.rope_n_pos = t.rope_n_pos;
   a.group = p.num_qo_heads / p.num_kv_heads;
@@ -190,21 +193,24 @@ const char* bsk_status_string(bsk_status status) {
 
 const char* bsk_last_error(void) { return g_err.c_str(); }
 
-bsk_status bsk_device_workers(int32_t tile_q, int32_t head_dim, int32_t dtype, int32_t* num_workers) {
+bsk_status bsk_device_workers(const bsk_problem* problem, int32_t* num_workers) {
   if (!num_workers) return fail(BSK_ERR_INVALID_ARG, "num_workers is NULL");
-  if (head_dim != 64 && head_dim != 128) return fail(BSK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!problem) return fail(BSK_ERR_INVALID_ARG, "problem is NULL");
+  if (problem->head_dim != 64 && problem->head_dim != 128) return fail(BSK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const bool dense = problem->kv_mode == BSK_KV_DENSE;
   const void* fn = nullptr;
   int threads = 0;
-  if (tile_q == BSK_TILE_DECODE) {
-    fn = bsk::decode_kernel_for_occupancy(dtype, head_dim);
+  if (problem->tile_q == BSK_TILE_DECODE) {
+    fn = bsk::decode_kernel_ptr(problem->dtype, problem->head_dim, dense, problem->rope_mode);
     threads = bsk::decode_threads();
-  } else if (tile_q == BSK_TILE_PREFILL) {
-    if (dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
-    fn = bsk::prefill_kernel_for_occupancy(head_dim);
+  } else if (problem->tile_q == BSK_TILE_PREFILL) {
+    if (problem->dtype == BSK_DTYPE_BF16 && problem->rope_mode == BSK_ROPE_NONE)
+      fn = bsk::prefill_kernel_ptr(problem->head_dim, dense);
     threads = bsk::prefill_threads();
   } else {
     return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 or 128");
   }
+  if (!fn) return fail(BSK_ERR_UNSUPPORTED, "no kernel built for this dtype / layout / RoPE combination");
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -273,7 +279,7 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
 }
 
 bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
-                          const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
+                          void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
   bsk_status s = check_run(problem, info, t, int_ws_dev, float_ws, float_ws_bytes, BSK_TILE_DECODE);
   if (s != BSK_OK) return s;
   if (problem->rope_mode != BSK_ROPE_NONE && problem->dtype != BSK_DTYPE_BF16)
@@ -288,7 +294,7 @@ bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info,
 }
 
 bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
-                           const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
+                           void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
   bsk_status s = check_run(problem, info, t, int_ws_dev, float_ws, float_ws_bytes, BSK_TILE_PREFILL);
   if (s != BSK_OK) return s;
   if (problem->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
@@ -319,7 +325,10 @@ bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* inf
   a.lse_st = t->lse_stride_tok;
   a.group = problem->num_qo_heads / problem->num_kv_heads;
   a.out_bf16 = problem->out_dtype == BSK_DTYPE_BF16;
-  int grid = problem->max_merge < 1 ? 1 : (problem->max_merge > 2048 ? 2048 : problem->max_merge);
+  // fixed grid: enough blocks for every (entry, row) pair of a full merge table, capped
+  const int64_t rows_per_block = 256 / (problem->head_dim / 4);
+  const int64_t want = (int64_t(problem->max_merge) * problem->tile_q + rows_per_block - 1) / rows_per_block;
+  const int grid = int(want < 1 ? 1 : (want > 4096 ? 4096 : want));
   hipError_t e = bsk::launch_merge(problem->head_dim, a, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return BSK_OK;

@@ -27,6 +27,98 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Merge of one (row, 4 columns) of a split unit from its chunks' partial
+// states: M = max_c LSE_c, w_c = exp(LSE_c - M), O = sum_c w_c O_c / sum_c w_c,
+// LSE = M + ln sum_c w_c; every chunk empty gives O = 0, LSE = -inf.  Writes
+// the output row (and the LSE when c4 == 0).
+template <int D>
+__device__ __forceinline__ void merge_row(const int32_t* rec, int rr, int c4, int tile_q,
+                                          const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                          int q0, int g, void* out, int64_t o_st, int64_t o_sh, float* lse_out,
+                                          int64_t lse_st, int out_bf16) {
+  const int h = rec[MG_H], row_lo = rec[MG_ROW_LO];
+  const int first = rec[MG_FIRST_SLOT], nc = rec[MG_N];
+  const float* pl = part_lse + int64_t(first) * tile_q + rr;
+  const float* po = part_o + (int64_t(first) * tile_q + rr) * D + c4;
+  // one pass with a running max (the loads of different chunks are independent)
+  float M = -INFINITY, wsum = 0.f;
+  float4 o = {0, 0, 0, 0};
+#pragma unroll 4
+  for (int c = 0; c < nc; ++c) {
+    const float lc = pl[int64_t(c) * tile_q];
+    const float4 x = *reinterpret_cast<const float4*>(po + int64_t(c) * tile_q * D);
+    if (lc > M) {
+      const float sc = __expf(M - lc);  // 0 when M was -inf
+      o.x *= sc;
+      o.y *= sc;
+      o.z *= sc;
+      o.w *= sc;
+      wsum *= sc;
+      M = lc;
+    }
+    if (lc != -INFINITY) {
+      const float w = __expf(lc - M);
+      o.x += w * x.x;
+      o.y += w * x.y;
+      o.z += w * x.z;
+      o.w += w * x.w;
+      wsum += w;
+    }
+  }
+  float lse = -INFINITY;
+  if (wsum > 0.f) {
+    const float inv = 1.f / wsum;
+    o.x *= inv;
+    o.y *= inv;
+    o.z *= inv;
+    o.w *= inv;
+    lse = M + __logf(wsum);
+  }
+  const int row = row_lo + rr;
+  const int tok = q0 + row / g;
+  const int qhd = h * g + row % g;
+  const int64_t oo = int64_t(tok) * o_st + int64_t(qhd) * o_sh + c4;
+  if (out_bf16) {
+    uint2 pk2 = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+    *reinterpret_cast<uint2*>(static_cast<__bf16*>(out) + oo) = pk2;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + oo) = o;
+  }
+  if (c4 == 0) lse_out[int64_t(tok) * lse_st + qhd] = lse;
+}
+
+// Called by all threads of a workgroup right after they stored one chunk's
+// partial state (slot `slot`).  Publishes the partial, counts the chunk in
+// the unit's arrival counter, and if this was the unit's last chunk merges
+// the unit in place and resets the counter for the next run.
+template <int D>
+__device__ __forceinline__ void finish_split_chunk(const AttnArgs& a, int slot, int tid, int nthreads,
+                                                   int* s_flag) {
+  const int32_t* __restrict__ ws = a.ws;
+  __threadfence();  // release this workgroup's partial-state stores device-wide
+  __syncthreads();
+  const int m = ws[ws[HDR_OFF_SLOTMAP] + slot];
+  const int32_t* rec = ws + ws[HDR_OFF_MERGE] + int64_t(m) * MERGE_WORDS;
+  if (tid == 0) {
+    int32_t* cnt = a.ws_rw + ws[HDR_OFF_COUNT] + m;
+    const int prev = atomicAdd(cnt, 1);
+    const int last = prev == rec[MG_N] - 1;
+    if (last) atomicExch(cnt, 0);
+    *s_flag = last;
+  }
+  __syncthreads();
+  if (*s_flag) {
+    __threadfence();  // acquire: the other chunks' partial states are visible
+    const int tile_q = ws[HDR_TILE_Q];
+    const int q0 = (ws + ws[HDR_OFF_QO])[rec[MG_R]];
+    const int nrows = rec[MG_ROW_HI] - rec[MG_ROW_LO];
+    for (int e = tid; e < nrows * (D / 4); e += nthreads)
+      merge_row<D>(rec, e / (D / 4), (e % (D / 4)) * 4, tile_q, a.part_o, a.part_lse, q0, a.group, a.out, a.o_st,
+                   a.o_sh, a.lse, a.lse_st, a.out_bf16);
+  }
+  __syncthreads();
+}
+
 // Key visibility for a query at position qpos: causal, then sliding window
 // or one of the first `sink` tokens.
 __device__ __forceinline__ bool key_visible(int t, int qpos, int causal, int window, int sink) {

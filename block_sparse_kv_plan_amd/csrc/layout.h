@@ -14,6 +14,10 @@
 //   [hdr[HDR_OFF_QO], ...)    qo_indptr[batch+1]
 //   [hdr[HDR_OFF_KVLEN], ...) kv_len[batch]
 //   [hdr[HDR_OFF_KVIND], ...) kv_indptr[batch+1] (page offsets or dense token offsets)
+//   [hdr[HDR_OFF_SLOTMAP], ...) slot_merge[num_slots]: merge entry of each partial slot
+//   [hdr[HDR_OFF_COUNT], ...) arrivals[num_merge]: chunks of each split unit that have
+//                             finished in the current run; zero in the uploaded plan and
+//                             reset to zero by the chunk that completes the unit
 #pragma once
 
 namespace bsk {
@@ -33,6 +37,8 @@ enum : int {
   HDR_OFF_KVIND = 11,
   HDR_MAX_KV_LEN = 12,
   HDR_MAX_QO_LEN = 13,
+  HDR_OFF_SLOTMAP = 14,
+  HDR_OFF_COUNT = 15,
   HDR_WORDS = 16,
 };
 

@@ -16,55 +16,28 @@ namespace bsk {
 
 constexpr int kMergeThreads = 256;
 
-// Plan-driven merge: fixed grid; block b takes merge entries b, b + grid, ...
-// Threads cover (row, 4 columns) pairs of an entry.
+// Plan-driven merge: fixed grid.  Work is spread over (merge entry, row)
+// pairs -- D/4 threads per row, each owning four columns -- so a few long
+// entries (a prefix split into many chunks) still use the whole chip.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  constexpr int TPR = D / 4;                  // threads per row
+  constexpr int RPB = kMergeThreads / TPR;    // rows per block per pass
   const int32_t* __restrict__ ws = a.ws;
   const int n_merge = ws[HDR_NUM_MERGE];
   const int tile_q = ws[HDR_TILE_Q];
   const int32_t* __restrict__ table = ws + ws[HDR_OFF_MERGE];
   const int32_t* __restrict__ qo_indptr = ws + ws[HDR_OFF_QO];
   const int g = a.group;
-  for (int m = blockIdx.x; m < n_merge; m += gridDim.x) {
+  const int c4 = (threadIdx.x % TPR) * 4;
+  const int64_t n_virtual = int64_t(n_merge) * tile_q;  // (entry, row-in-tile) pairs
+  for (int64_t v = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR; v < n_virtual; v += int64_t(gridDim.x) * RPB) {
+    const int m = int(v / tile_q);
+    const int rr = int(v % tile_q);
     const int32_t* rec = table + int64_t(m) * MERGE_WORDS;
-    const int r = rec[MG_R], h = rec[MG_H], row_lo = rec[MG_ROW_LO], row_hi = rec[MG_ROW_HI];
-    const int first = rec[MG_FIRST_SLOT], nc = rec[MG_N];
-    const int q0 = qo_indptr[r];
-    const int nrows = row_hi - row_lo;
-    for (int e = threadIdx.x; e < nrows * (D / 4); e += kMergeThreads) {
-      const int rr = e / (D / 4);
-      const int c4 = (e % (D / 4)) * 4;
-      float M = -INFINITY;
-      for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[int64_t(first + c) * tile_q + rr]);
-      float4 o = {0, 0, 0, 0};
-      float lse = -INFINITY;
-      if (M != -INFINITY) {
-        float wsum = 0.f;
-        for (int c = 0; c < nc; ++c) wsum += __expf(a.part_lse[int64_t(first + c) * tile_q + rr] - M);
-        lse = M + __logf(wsum);
-        for (int c = 0; c < nc; ++c) {
-          const int64_t s = int64_t(first + c) * tile_q + rr;
-          const float w = __expf(a.part_lse[s] - lse);
-          const float4 x = *reinterpret_cast<const float4*>(a.part_o + s * D + c4);
-          o.x += w * x.x;
-          o.y += w * x.y;
-          o.z += w * x.z;
-          o.w += w * x.w;
-        }
-      }
-      const int row = row_lo + rr;
-      const int tok = q0 + row / g;
-      const int qhd = h * g + row % g;
-      const int64_t oo = int64_t(tok) * a.o_st + int64_t(qhd) * a.o_sh + c4;
-      if (a.out_bf16) {
-        uint2 pk2 = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-        *reinterpret_cast<uint2*>(static_cast<__bf16*>(a.out) + oo) = pk2;
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oo) = o;
-      }
-      if (c4 == 0) a.lse[int64_t(tok) * a.lse_st + qhd] = lse;
-    }
+    if (rr >= rec[MG_ROW_HI] - rec[MG_ROW_LO]) continue;
+    merge_row<D>(rec, rr, c4, tile_q, a.part_o, a.part_lse, qo_indptr[rec[MG_R]], g, a.out, a.o_st, a.o_sh, a.lse,
+                 a.lse_st, a.out_bf16);
   }
 }
 

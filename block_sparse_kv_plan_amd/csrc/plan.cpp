@@ -53,21 +53,26 @@ namespace bsk {
 namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kWorkerBits = 20;  // the LPT heap packs (load, worker) into 64 bits
+constexpr uint64_t kWorkerMask = (uint64_t(1) << kWorkerBits) - 1;
 inline int64_t align4(int64_t x) { return (x + 3) & ~int64_t(3); }
 
 struct Layout {
-  int64_t off_items, off_merge, off_qo, off_kvlen, off_kvind, total_words;
+  int64_t off_items, off_merge, off_qo, off_kvlen, off_kvind, off_slotmap, off_count, total_words;
 };
 
-// Word offsets for a plan with `n_items` items and `n_merge` merge entries.
-Layout layout_for(int32_t W, int64_t n_items, int64_t n_merge, int32_t batch) {
+// Word offsets for a plan with `n_items` items, `n_merge` merge entries and `n_slots` slots.
+Layout layout_for(int32_t W, int64_t n_items, int64_t n_merge, int64_t n_slots, int32_t batch) {
   Layout L;
   L.off_items = align4(HDR_WORDS + int64_t(W) + 1);
   L.off_merge = L.off_items + n_items * ITEM_WORDS;
   L.off_qo = L.off_merge + n_merge * MERGE_WORDS;
   L.off_kvlen = L.off_qo + batch + 1;
   L.off_kvind = L.off_kvlen + batch;
-  L.total_words = L.off_kvind + batch + 1;
+  L.off_slotmap = L.off_kvind + batch + 1;
+  L.off_count = L.off_slotmap + n_slots;
+  L.total_words = L.off_count + n_merge;
   return L;
 }
 
@@ -75,11 +80,34 @@ struct Unit {
   int32_t r, h, row_lo, row_hi, lo, hi, sink_hi;
 };
 
+struct Item {
+  int32_t r, h, row_lo, row_hi, kv_lo, kv_hi, slot;
+  int64_t cost;
+};
+
+// Binary min-heap of unique 64-bit keys with a combined pop-and-push: the
+// root is replaced by a larger key and sifted down (child choice is
+// branch-free; the key usually sinks to the bottom, so the exit test is
+// well predicted).
+inline void sift_down(uint64_t* h, int32_t n, int32_t i) {
+  const uint64_t key = h[i];
+  for (;;) {
+    int32_t c = 2 * i + 1;
+    if (c >= n) break;
+    const int32_t c2 = c + 1;
+    c += (c2 < n) & (h[c2 < n ? c2 : c] < h[c]);
+    if (h[c] >= key) break;
+    h[i] = h[c];
+    i = c;
+  }
+  h[i] = key;
+}
+
 }  // namespace
 
 size_t plan_workspace_bytes(const PlanParams& p) {
   const int64_t max_items = int64_t(p.num_workers) * p.max_items_per_worker;
-  Layout L = layout_for(p.num_workers, max_items, p.max_merge, p.max_batch);
+  Layout L = layout_for(p.num_workers, max_items, p.max_merge, p.max_slots, p.max_batch);
   return size_t(L.total_words) * sizeof(int32_t);
 }
 
@@ -94,6 +122,7 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     return fail(PLAN_INVALID, "num_qo_heads must be a positive multiple of num_kv_heads");
   if (p.tile_q <= 0 || p.tile_kv <= 0 || p.num_workers <= 0 || p.split_factor <= 0)
     return fail(PLAN_INVALID, "tile_q, tile_kv, num_workers and split_factor must be positive");
+  if (p.num_workers > int32_t(kWorkerMask)) return fail(PLAN_INVALID, "num_workers must be below 2^20");
   if (p.min_chunk <= 0 || p.min_chunk % p.tile_kv != 0)
     return fail(PLAN_INVALID, "min_chunk must be a positive multiple of tile_kv");
   if (p.max_chunk < 0 || (p.max_chunk > 0 && (p.max_chunk % p.tile_kv != 0 || p.max_chunk < p.min_chunk)))
@@ -118,8 +147,9 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     max_qo = std::max<int32_t>(max_qo, int32_t(Q));
   }
 
-  // 1. units
-  std::vector<Unit> units;
+  // 1. units (scratch containers are kept per thread across calls)
+  thread_local std::vector<Unit> units;
+  units.clear();
   for (int32_t r = 0; r < batch; ++r) {
     const int32_t Q = qo_indptr[r + 1] - qo_indptr[r];
     const int32_t L = kv_len[r];
@@ -149,16 +179,16 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   Lc = std::max<int64_t>(p.min_chunk, Lc);
   if (p.max_chunk > 0) Lc = std::min<int64_t>(Lc, p.max_chunk);
   if (Lc > INT32_MAX) return fail(PLAN_INVALID, "chunk length overflows int32");
+  if (C + int64_t(p.item_overhead) * (C / p.tile_kv + int64_t(units.size()) * 2 + 1) >= (int64_t(1) << 42))
+    return fail(PLAN_INVALID, "total work too large for the planner's load counters");
 
   // 4-5. chunks -> items, slots, merge entries
-  struct Item {
-    int32_t r, h, row_lo, row_hi, kv_lo, kv_hi, slot;
-    int64_t cost;
-  };
-  std::vector<Item> items;
-  std::vector<std::array<int32_t, 6>> merges;
+  thread_local std::vector<Item> items;
+  thread_local std::vector<std::array<int32_t, 6>> merges;
+  items.clear();
+  merges.clear();
   int64_t next_slot = 0;
-  std::vector<std::pair<int32_t, int32_t>> chunks;
+  thread_local std::vector<std::pair<int32_t, int32_t>> chunks;
   for (const Unit& u : units) {
     chunks.clear();
     for (int64_t k = u.lo / Lc; k <= (int64_t(u.hi) - 1) / Lc; ++k)
@@ -188,32 +218,66 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   if (int64_t(items.size()) > int64_t(W) * p.max_items_per_worker)
     return fail(PLAN_CAPACITY, "more items than num_workers * max_items_per_worker");
 
-  // 6. LPT assignment
-  std::vector<int32_t> order(items.size());
-  for (size_t i = 0; i < order.size(); ++i) order[i] = int32_t(i);
-  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    if (items[a].cost != items[b].cost) return items[a].cost > items[b].cost;
-    return a < b;
-  });
-  using Slot = std::pair<int64_t, int32_t>;
-  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-  for (int32_t w = 0; w < W; ++w) heap.push({0, w});
-  std::vector<std::vector<int32_t>> lists(W);
-  std::vector<int64_t> load(W, 0);
-  for (int32_t id : order) {
-    Slot s = heap.top();
-    heap.pop();
-    lists[s.second].push_back(id);
-    load[s.second] = s.first + items[id].cost;
-    heap.push({load[s.second], s.second});
+  // 6. LPT assignment (flat arrays; the per-worker lists are built as CSR
+  //    afterwards, each in assignment order)
+  thread_local std::vector<int32_t> order, assign, counts, bucket;
+  thread_local std::vector<uint64_t> heap;
+  const int32_t n_items = int32_t(items.size());
+  // order = items by (cost desc, id asc): a stable counting sort on cost
+  // (costs are bounded by the chunk length plus the overhead)
+  int64_t max_cost = 0;
+  for (const Item& it : items) max_cost = std::max(max_cost, it.cost);
+  bucket.assign(size_t(max_cost) + 2, 0);
+  for (const Item& it : items) ++bucket[size_t(max_cost - it.cost)];
+  int32_t run = 0;
+  for (size_t c = 0; c < bucket.size(); ++c) {
+    const int32_t k = bucket[c];
+    bucket[c] = run;
+    run += k;
+  }
+  order.resize(n_items);
+  for (int32_t i = 0; i < n_items; ++i) order[size_t(bucket[size_t(max_cost - items[i].cost)]++)] = i;
+  assign.resize(n_items);
+  counts.assign(W + 1, 0);
+  thread_local std::vector<int64_t> load;
+  load.assign(W, 0);
+  // All workers start at load 0 and ties go to the lower worker, so the
+  // leading run of items with the largest cost is dealt round-robin: after
+  // every full round all loads are equal again.  Exactly what the heap
+  // would produce, without its per-item cost.
+  int32_t k = 0;
+  if (n_items > 0) {
+    const int64_t c0 = items[order[0]].cost;
+    while (k < n_items && items[order[k]].cost == c0) {
+      const int32_t w = k % W;
+      assign[k] = w;
+      ++counts[w];
+      load[w] += c0;
+      ++k;
+    }
+  }
+  // the rest: min-heap of (load, worker) packed as load << 20 | worker, so one
+  // integer comparison gives the lexicographic (load, worker) order
+  heap.resize(W);
+  for (int32_t w = 0; w < W; ++w) heap[w] = (uint64_t(load[w]) << kWorkerBits) | uint64_t(w);
+  std::make_heap(heap.begin(), heap.end(), std::greater<uint64_t>());
+  for (; k < n_items; ++k) {
+    const uint64_t top = heap[0];
+    const int32_t w = int32_t(top & kWorkerMask);
+    const int32_t id = order[k];
+    assign[k] = w;
+    ++counts[w];
+    heap[0] = top + (uint64_t(items[id].cost) << kWorkerBits);
+    load[w] = int64_t(heap[0] >> kWorkerBits);
+    sift_down(heap.data(), W, 0);
   }
   int32_t max_on_worker = 0;
-  for (const auto& l : lists) max_on_worker = std::max<int32_t>(max_on_worker, int32_t(l.size()));
+  for (int32_t w = 0; w < W; ++w) max_on_worker = std::max(max_on_worker, counts[w]);
   if (max_on_worker > p.max_items_per_worker)
     return fail(PLAN_CAPACITY, "more items on one worker than max_items_per_worker");
 
   // 7. serialise
-  const Layout L = layout_for(W, int64_t(items.size()), int64_t(merges.size()), batch);
+  const Layout L = layout_for(W, int64_t(items.size()), int64_t(merges.size()), next_slot, batch);
   std::memset(buf, 0, size_t(L.total_words) * sizeof(int32_t));
   buf[HDR_NUM_ITEMS] = int32_t(items.size());
   buf[HDR_NUM_MERGE] = int32_t(merges.size());
@@ -229,30 +293,32 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   buf[HDR_OFF_KVIND] = int32_t(L.off_kvind);
   buf[HDR_MAX_KV_LEN] = max_kv;
   buf[HDR_MAX_QO_LEN] = max_qo;
+  buf[HDR_OFF_SLOTMAP] = int32_t(L.off_slotmap);
+  buf[HDR_OFF_COUNT] = int32_t(L.off_count);
   int32_t* wptr = buf + HDR_WORDS;
   int32_t* out = buf + L.off_items;
-  int32_t pos = 0;
-  for (int32_t w = 0; w < W; ++w) {
-    wptr[w] = pos;
-    for (int32_t id : lists[w]) {
-      const Item& it = items[id];
-      int32_t* rec = out + int64_t(pos) * ITEM_WORDS;
-      rec[IT_R] = it.r;
-      rec[IT_H] = it.h;
-      rec[IT_ROW_LO] = it.row_lo;
-      rec[IT_ROW_HI] = it.row_hi;
-      rec[IT_KV_LO] = it.kv_lo;
-      rec[IT_KV_HI] = it.kv_hi;
-      rec[IT_SLOT] = it.slot;
-      rec[IT_ID] = id;
-      ++pos;
-    }
+  wptr[0] = 0;
+  for (int32_t w = 0; w < W; ++w) wptr[w + 1] = wptr[w] + counts[w];
+  for (int32_t w = 0; w < W; ++w) counts[w] = wptr[w];  // reuse as fill cursors
+  for (int32_t k = 0; k < n_items; ++k) {
+    const int32_t id = order[k];
+    const Item& it = items[id];
+    int32_t* rec = out + int64_t(counts[assign[k]]++) * ITEM_WORDS;
+    rec[IT_R] = it.r;
+    rec[IT_H] = it.h;
+    rec[IT_ROW_LO] = it.row_lo;
+    rec[IT_ROW_HI] = it.row_hi;
+    rec[IT_KV_LO] = it.kv_lo;
+    rec[IT_KV_HI] = it.kv_hi;
+    rec[IT_SLOT] = it.slot;
+    rec[IT_ID] = id;
   }
-  wptr[W] = pos;
   for (size_t m = 0; m < merges.size(); ++m) {
     int32_t* rec = buf + L.off_merge + int64_t(m) * MERGE_WORDS;
     for (int k = 0; k < 6; ++k) rec[k] = merges[m][k];
+    for (int32_t c = 0; c < merges[m][5]; ++c) buf[L.off_slotmap + merges[m][4] + c] = int32_t(m);
   }
+  // arrival counters stay zero (memset above)
   for (int32_t r = 0; r <= batch; ++r) buf[L.off_qo + r] = batch ? qo_indptr[r] : 0;
   for (int32_t r = 0; r < batch; ++r) buf[L.off_kvlen + r] = kv_len[r];
   for (int32_t r = 0; r <= batch; ++r) buf[L.off_kvind + r] = batch ? kv_indptr[r] : 0;

@@ -40,6 +40,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void prefill_kernel(AttnArgs a) {
   __shared__ __align__(16) unsigned short s_k[kPreKeys * ROW];
   __shared__ __align__(16) unsigned short s_v[kPreKeys * ROW];
   __shared__ int32_t s_pages[DENSE ? 1 : kMaxPages];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -234,6 +235,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void prefill_kernel(AttnArgs a) {
         if (j == 0) a.part_lse[int64_t(slot) * kPreRows + rr] = lse;
       }
     }
+    if (slot >= 0 && a.fused_merge) finish_split_chunk<D>(a, slot, tid, kPreThreads, &s_last);
   }
 }
 
@@ -251,9 +253,12 @@ hipError_t launch_prefill(int head_dim, bool dense, const AttnArgs& a, int grid,
   return hipErrorInvalidValue;
 }
 
-const void* prefill_kernel_for_occupancy(int head_dim) {
-  return head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<64, false>)
-                        : reinterpret_cast<const void*>(&prefill_kernel<128, false>);
+const void* prefill_kernel_ptr(int head_dim, bool dense) {
+  if (head_dim == 128) return dense ? reinterpret_cast<const void*>(&prefill_kernel<128, true>)
+                                    : reinterpret_cast<const void*>(&prefill_kernel<128, false>);
+  if (head_dim == 64) return dense ? reinterpret_cast<const void*>(&prefill_kernel<64, true>)
+                                   : reinterpret_cast<const void*>(&prefill_kernel<64, false>);
+  return nullptr;
 }
 
 int prefill_threads() { return kPreThreads; }

@@ -88,7 +88,9 @@ typedef struct bsk_problem {
   int32_t window;        /* > 0: key j visible only if qpos - j < window ...   */
   int32_t sink;          /* ... or j < sink (attention sinks); window <= 0: off */
   int32_t rope_mode;     /* BSK_ROPE_*; rotate-half, q and k both rotated      */
-  int32_t reserved0;
+  int32_t fused_merge;   /* 1: run merges split units in-kernel (the chunk that
+                            finishes a unit last combines it); 0: run leaves
+                            partial states for bsk_merge_states              */
   double rope_theta;     /* RoPE base                                          */
   float sm_scale;        /* logit scale, e.g. 1/sqrt(head_dim)                 */
   /* plan parameters (see bsk_plan) */
@@ -156,13 +158,16 @@ const char* bsk_status_string(bsk_status status);
 const char* bsk_last_error(void);
 
 /*
- * Persistent-grid size for a kernel class on the current device: compute
- * units times resident workgroups per CU for the tile class (tile_q 16 or
- * 128), head_dim and dtype.  The grid must not exceed what is co-resident
- * (a persistent launch larger than that is what [FI-PR5329, review] reports
- * failing).  Needs a GPU.
+ * Persistent-grid size for `problem` on the current device: compute units
+ * times the workgroups of the exact kernel variant the problem selects
+ * (query-tile class, dtype, head_dim, KV layout, RoPE mode) that fit on one
+ * CU at once.  The persistent grid must not exceed what is co-resident (a
+ * persistent launch larger than that is what [FI-PR5329, review] reports
+ * failing; here it would run a second, unbalanced wave of workers).
+ * Only the shape fields of `problem` are read; plan fields may be unset.
+ * Needs a GPU.  Errors: INVALID_ARG, UNSUPPORTED, HIP.
  */
-bsk_status bsk_device_workers(int32_t tile_q, int32_t head_dim, int32_t dtype, int32_t* num_workers);
+bsk_status bsk_device_workers(const bsk_problem* problem, int32_t* num_workers);
 
 /*
  * Workspace sizes for `problem` ([FI-PR5329, code analysis 2]: float and int
@@ -186,9 +191,10 @@ bsk_status bsk_workspace_query(const bsk_problem* problem, size_t* int_ws_bytes,
  * max(min_chunk, roundup(ceil(total_cost / (num_workers * split_factor)),
  * tile_kv)) keys at absolute multiples of L_c (plus the sink range as its own
  * chunk), and items are assigned longest-first to the least-loaded worker.
- * Multi-chunk units write partial states to float-workspace slots that
- * bsk_merge_states combines.  The exact rules, tie-breaks included, are
- * spelled out at the top of csrc/plan.cpp.
+ * Multi-chunk units write partial states to float-workspace slots; they
+ * are combined in-kernel (problem.fused_merge = 1) or by bsk_merge_states.
+ * The exact rules, tie-breaks included, are spelled out at the top of
+ * csrc/plan.cpp.
  * host_ws receives the plan; if int_ws_dev is non-NULL its first used_bytes
  * are then copied there with one hipMemcpyAsync on `stream` (host_ws must
  * stay untouched until that copy completes).  int_ws_dev == NULL plans on
@@ -208,14 +214,18 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
  * from the int workspace; page ids of an item are staged in LDS; K/V pages
  * are read with coalesced 16-byte loads; logits and P.V use MFMA (bf16) or
  * fp32 MFMA (f32 inputs); online softmax in fp32.  Single-chunk items write
- * out/lse; multi-chunk items write partial (O, LSE) to float_ws.
+ * out/lse; multi-chunk items write partial (O, LSE) to float_ws, and with
+ * problem.fused_merge = 1 the chunk that completes a unit (counted with a
+ * device-scope atomic in the int workspace, which the run therefore
+ * updates; the counters are back at zero when the run ends) merges it
+ * into out/lse.  Concurrent runs must not share one int workspace.
  * RoPE (bf16 only): q and every key are rotated in-kernel from the
  * cos/sin table (K stays unrotated in the cache); STREAMING needs qo_len 1.
  * Errors: INVALID_ARG (plan/tile mismatch, null pointers), UNSUPPORTED
  * (head_dim, dtype, rope with f32), WORKSPACE, HIP (launch failure).
  */
 bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
-                          const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
+                          void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
 
 /*
  * Large-tile attention (128 query rows per item): ragged (causal) prefill,
@@ -226,15 +236,16 @@ bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info,
  * bsk_run_decode.  Errors as bsk_run_decode (no RoPE).
  */
 bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
-                           const void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
+                           void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
 
 /*
  * Combine the partial states of every multi-chunk unit of the plan
  * ([FI-0.6, kernel types: split-KV]): per query row,
  * LSE = M + ln sum_c exp(LSE_c - M) with M = max_c LSE_c, and
  * O = sum_c exp(LSE_c - LSE) * O_c, written to t->out / t->lse.  Rows of
- * single-chunk units are left untouched (already written by run).  Fixed
- * grid.  Errors: INVALID_ARG, HIP.
+ * single-chunk units are left untouched (already written by run).  Needed
+ * after a run with problem.fused_merge = 0; after a fused run it recomputes
+ * the same values.  Fixed grid.  Errors: INVALID_ARG, HIP.
  */
 bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                             const void* int_ws_dev, const void* float_ws, void* stream);

@@ -21,4 +21,6 @@ def decode(buf) -> dict:
         "merge": merge,
         "qo_indptr": w[off_qo:off_qo + batch + 1], "kv_len": w[off_kvlen:off_kvlen + batch],
         "kv_indptr": w[off_kvind:off_kvind + batch + 1],
+        "slot_merge": w[int(w[14]):int(w[14]) + n_slots],
+        "arrivals": w[int(w[15]):int(w[15]) + n_merge],
     }

@@ -168,6 +168,29 @@ def test_determinism_and_page_permutation():
     compare(b1, O1, L1)
 
 
+@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL])
+def test_fused_merge_matches_separate_merge(tile_q):
+    """In-kernel merge by the last chunk of each split unit gives exactly the
+    separate merge kernel's result, leaves the arrival counters at zero, and a
+    second run on the same plan (no re-plan) reproduces it."""
+    from tests import planbuf
+    kv = np.array([900, 2000, 33, 512])
+    qo = np.array([1, 1, 1, 1]) if tile_q == bsk.TILE_DECODE else np.array([100, 300, 33, 200])
+    b = small(90, kv, qo=qo, Hq=32, Hk=8, d=128, causal=True)
+    kw = dict(tile_q=tile_q, num_workers=32, split_factor=4, min_chunk=64)
+    O1, L1, _, _ = run(b, fused_merge=0, **kw)
+    O2, L2, attn, (t, out, lse, _, _) = run(b, fused_merge=1, **kw)
+    assert attn.info.num_merge > 0
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    compare(b, O2, L2)
+    arrivals = planbuf.decode(attn.int_ws.cpu().numpy())["arrivals"]
+    assert len(arrivals) == attn.info.num_merge and (arrivals == 0).all()
+    out.fill_(float("nan"))
+    attn.run(t)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.double().cpu().numpy(), O2) and np.array_equal(lse.double().cpu().numpy(), L2)
+
+
 # ------------------------------------------------------------------ prefill (128-row tiles)
 
 def test_prefill_small_several_tiles():
