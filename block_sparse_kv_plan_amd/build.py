@@ -45,7 +45,7 @@ def build(verbose: bool = False) -> str:
         jobs.append([HIPCC, f"--offload-arch={ARCH}", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, f"--offload-arch={ARCH}", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():

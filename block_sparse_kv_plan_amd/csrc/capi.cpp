@@ -59,7 +59,7 @@ bsk_status check_problem(const bsk_problem* p) {
   if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
     return fail(BSK_ERR_INVALID_ARG, "streaming RoPE positions need causal masking");
   if (p->rope_mode != BSK_ROPE_NONE && !(p->rope_theta > 1.0)) return fail(BSK_ERR_INVALID_ARG, "rope_theta must be > 1");
-  if (!std::isfinite(p->sm_scale)) return fail(BSK_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.f)) return fail(BSK_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (p->tile_q != BSK_TILE_DECODE && p->tile_q != BSK_TILE_PREFILL)
     return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 (decode) or 128 (prefill)");
   if (p->tile_kv <= 0 || (p->kv_mode == BSK_KV_PAGED && p->tile_kv % p->page_size != 0))

@@ -202,6 +202,7 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
       }
     }
 
+    const RowMask rm = row_mask(row_ok, qpos, kv_hi, a.causal, a.window, a.sink);
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[NACC];
 #pragma unroll
@@ -298,8 +299,7 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = tb + 4 * i + j;
-          const bool ok = row_ok && t >= kv_lo && t < kv_hi && key_visible(t, qpos, a.causal, a.window, a.sink);
-          sv[i] = ok ? st[i] * a.scale_log2 : -INFINITY;
+          sv[i] = (row_sees(rm, t) & (t >= kv_lo)) ? st[i] * a.scale_log2 : -INFINITY;
         }
         softmax_update(sv, p);
         u32x2 pw;
@@ -349,8 +349,7 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = tb + 4 * j + i;
-          const bool ok = row_ok && t >= kv_lo && t < kv_hi && key_visible(t, qpos, a.causal, a.window, a.sink);
-          sv[i] = ok ? st[i] * a.scale_log2 : -INFINITY;
+          sv[i] = (row_sees(rm, t) & (t >= kv_lo)) ? st[i] * a.scale_log2 : -INFINITY;
         }
         softmax_update(sv, p);
 #pragma unroll

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 #include "args.h"
 
 namespace bsk {
@@ -117,6 +119,27 @@ __device__ __forceinline__ void finish_split_chunk(const AttnArgs& a, int slot, 
                    a.o_sh, a.lse, a.lse_st, a.out_bf16);
   }
   __syncthreads();
+}
+
+// Visible keys of one query row as integer bounds, so that each key's test
+// is a few compares and a select (no per-key branches): key t is visible iff
+// t < hi and (t >= lo or t < sink_hi).  Keys past the item's range, the
+// causal bound and the sliding window (with its sinks) fold into the bounds;
+// a row outside the tile sees nothing.
+struct RowMask {
+  int lo, hi, sink_hi;
+};
+
+__device__ __forceinline__ RowMask row_mask(bool row_ok, int qpos, int kv_hi, int causal, int window, int sink) {
+  RowMask m;
+  m.hi = row_ok ? (causal ? min(kv_hi, qpos + 1) : kv_hi) : INT_MIN;
+  m.lo = window > 0 ? qpos - window + 1 : INT_MIN;
+  m.sink_hi = window > 0 ? sink : INT_MIN;
+  return m;
+}
+
+__device__ __forceinline__ bool row_sees(const RowMask& m, int t) {
+  return (t < m.hi) & ((t >= m.lo) | (t < m.sink_hi));
 }
 
 // Key visibility for a query at position qpos: causal, then sliding window
