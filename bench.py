@@ -209,6 +209,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="profiling aid: run just this workload (decode|prefill|composable|rope)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="profiling aid: first run one plain device copy of this many MiB, the reference that "
+                         "scales hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU "
@@ -223,6 +226,13 @@ def main():
 
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
     result = {}
     secondary = {}
 
