@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="profiling aid: run just this workload (decode|prefill|composable|rope)")
+    ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
+                    help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
@@ -284,7 +286,7 @@ def main():
         log("prefill: ragged causal prefill with append")
         b = W.ragged_prefill()
         flops, pairs = prefill_flops(b)
-        runner = Runner(b, bsk.TILE_PREFILL, copies=1, device=device)
+        runner = Runner(b, args.prefill_tile, copies=1, device=device)
         m = timed(runner, max(5, args.steps // 5), 3)
         tf = flops / m["kernel_s_mean"] / 1e12
         secondary["ragged_prefill"] = {
@@ -292,7 +294,8 @@ def main():
                         "uniform [0,2048] cached keys, 32q/8kv, d128",
             "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 1), "step_ms": round(m["wall_s"] * 1e3, 3),
-            "unmasked_pairs": pairs, "flops": flops}
+            "unmasked_pairs": pairs, "flops": flops, "tile_q": args.prefill_tile,
+            "num_workers": runner.attn[0].info.num_workers, "items": runner.attn[0].info.num_items}
         del runner
         torch.cuda.empty_cache()
 
@@ -316,7 +319,7 @@ def main():
         log("composable: shared 16384-token dense prefix + 64 paged suffixes")
         c = W.shared_prefix()
         from block_sparse_kv_plan_amd.attention import merge_pair
-        pre = Runner(c.prefix, bsk.TILE_PREFILL, copies=1, device=device)
+        pre = Runner(c.prefix, args.prefill_tile, copies=1, device=device)
         suf = Runner(c.suffix, bsk.TILE_DECODE, copies=1, device=device)
         fin_o = torch.empty_like(suf.out)
         fin_l = torch.empty_like(suf.lse)

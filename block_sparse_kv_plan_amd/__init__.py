@@ -24,7 +24,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 KV_PAGED, KV_DENSE = 0, 1
 ROPE_NONE, ROPE_STREAMING, ROPE_ABSOLUTE = 0, 1, 2
-TILE_DECODE, TILE_PREFILL = 16, 128
+TILE_DECODE, TILE_PREFILL, TILE_PREFILL_256 = 16, 128, 256
 
 i32, i64, f32, f64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 

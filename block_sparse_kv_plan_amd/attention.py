@@ -11,7 +11,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (DTYPE_BF16, DTYPE_F32, KV_DENSE, KV_PAGED, ROPE_NONE, TILE_DECODE, TILE_PREFILL, PlanInfo,
+from . import (DTYPE_BF16, DTYPE_F32, KV_DENSE, KV_PAGED, ROPE_NONE, TILE_DECODE, TILE_PREFILL, TILE_PREFILL_256, PlanInfo,
                Problem, Tensors, device_workers, merge_state_pair, merge_states, plan, run_decode, run_prefill,
                workspace_query)
 
@@ -21,6 +21,7 @@ TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
 DEFAULTS = {
     TILE_DECODE: dict(tile_kv=16, split_factor=2, min_chunk=128, max_items_per_worker=64),
     TILE_PREFILL: dict(tile_kv=64, split_factor=1, min_chunk=256, max_items_per_worker=64),
+    TILE_PREFILL_256: dict(tile_kv=64, split_factor=1, min_chunk=256, max_items_per_worker=64),
 }
 
 

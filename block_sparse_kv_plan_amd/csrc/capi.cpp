@@ -33,6 +33,8 @@ int ilog2(int x) {
   return s;
 }
 
+bool is_prefill_tile(int tile_q) { return tile_q == BSK_TILE_PREFILL || tile_q == BSK_TILE_PREFILL_256; }
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Largest chunk (keys) whose page ids fit the kernels' LDS page list.
@@ -60,8 +62,8 @@ bsk_status check_problem(const bsk_problem* p) {
     return fail(BSK_ERR_INVALID_ARG, "streaming RoPE positions need causal masking");
   if (p->rope_mode != BSK_ROPE_NONE && !(p->rope_theta > 1.0)) return fail(BSK_ERR_INVALID_ARG, "rope_theta must be > 1");
   if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.f)) return fail(BSK_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
-  if (p->tile_q != BSK_TILE_DECODE && p->tile_q != BSK_TILE_PREFILL)
-    return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 (decode) or 128 (prefill)");
+  if (p->tile_q != BSK_TILE_DECODE && !is_prefill_tile(p->tile_q))
+    return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 (decode) or 128 / 256 (prefill)");
   if (p->tile_kv <= 0 || (p->kv_mode == BSK_KV_PAGED && p->tile_kv % p->page_size != 0))
     return fail(BSK_ERR_INVALID_ARG, "tile_kv must be a positive multiple of page_size");
   if (p->num_workers <= 0 || p->split_factor <= 0) return fail(BSK_ERR_INVALID_ARG, "num_workers, split_factor");
@@ -108,7 +110,8 @@ bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_
   bsk_status s = check_problem(p);
   if (s != BSK_OK) return s;
   if (!info || !t || !int_ws) return fail(BSK_ERR_INVALID_ARG, "plan info, tensors and int workspace are required");
-  if (p->tile_q != tile_q || info->tile_q != tile_q)
+  const bool want_prefill = tile_q != BSK_TILE_DECODE;
+  if ((want_prefill ? !is_prefill_tile(p->tile_q) : p->tile_q != tile_q) || info->tile_q != p->tile_q)
     return fail(BSK_ERR_INVALID_ARG, "plan was built for the other query-tile class");
   if (info->num_workers != p->num_workers) return fail(BSK_ERR_INVALID_ARG, "plan info does not match problem");
   if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*p)))
@@ -203,12 +206,12 @@ bsk_status bsk_device_workers(const bsk_problem* problem, int32_t* num_workers) 
   if (problem->tile_q == BSK_TILE_DECODE) {
     fn = bsk::decode_kernel_ptr(problem->dtype, problem->head_dim, dense, problem->rope_mode);
     threads = bsk::decode_threads();
-  } else if (problem->tile_q == BSK_TILE_PREFILL) {
+  } else if (is_prefill_tile(problem->tile_q)) {
     if (problem->dtype == BSK_DTYPE_BF16 && problem->rope_mode == BSK_ROPE_NONE)
-      fn = bsk::prefill_kernel_ptr(problem->head_dim, dense);
+      fn = bsk::prefill_kernel_ptr(problem->head_dim, dense, problem->tile_q);
     threads = bsk::prefill_threads();
   } else {
-    return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16 or 128");
+    return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16, 128 or 256");
   }
   if (!fn) return fail(BSK_ERR_UNSUPPORTED, "no kernel built for this dtype / layout / RoPE combination");
   int dev = 0, cus = 0, per_cu = 0;
@@ -299,9 +302,23 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
   if (s != BSK_OK) return s;
   if (problem->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
   if (problem->rope_mode != BSK_ROPE_NONE) return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for decode only");
+  // the kernel forms page addresses with a 32 x 32 -> 64-bit multiply of the page id and the byte stride
+  // and keeps a row's head / in-page (dense: in-tile) offset in 32 bits
+  if (problem->kv_mode == BSK_KV_PAGED &&
+      (t->k_stride_page < 0 || t->v_stride_page < 0 || t->k_stride_page > INT32_MAX || t->v_stride_page > INT32_MAX))
+    return fail(BSK_ERR_INVALID_ARG, "page strides must be in [0, 2^31) elements");
+  {
+    const int64_t rows = problem->kv_mode == BSK_KV_PAGED ? std::min(problem->page_size, 64) : 64;
+    const int64_t hk = problem->num_kv_heads;
+    const int64_t kspan = (hk - 1) * t->k_stride_head + (rows - 1) * t->k_stride_tok + problem->head_dim;
+    const int64_t vspan = (hk - 1) * t->v_stride_head + (rows - 1) * t->v_stride_tok + problem->head_dim;
+    if (t->k_stride_head < 0 || t->k_stride_tok < 0 || t->v_stride_head < 0 || t->v_stride_tok < 0 ||
+        kspan > INT32_MAX || vspan > INT32_MAX)
+      return fail(BSK_ERR_INVALID_ARG, "head / token strides too large for the prefill kernel's 32-bit row offsets");
+  }
   const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
-  hipError_t e = bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, a, info->num_workers,
-                                     static_cast<hipStream_t>(stream));
+  hipError_t e = bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, problem->tile_q, a,
+                                     info->num_workers, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return BSK_OK;
 }

@@ -25,8 +25,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round-to-nearest-even;
+// one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Merge of one (row, 4 columns) of a split unit from its chunks' partial

@@ -12,8 +12,8 @@ hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, const At
 const void* decode_kernel_ptr(int dtype, int head_dim, bool dense, int rope);
 int decode_threads();
 
-hipError_t launch_prefill(int head_dim, bool dense, const AttnArgs& a, int grid, hipStream_t stream);
-const void* prefill_kernel_ptr(int head_dim, bool dense);
+hipError_t launch_prefill(int head_dim, bool dense, int tile_q, const AttnArgs& a, int grid, hipStream_t stream);
+const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q);
 int prefill_threads();
 
 hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t stream);

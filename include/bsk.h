@@ -64,8 +64,10 @@ typedef int32_t bsk_status;
 #define BSK_ROPE_STREAMING 1 /* key position = rank in the query's visible set */
 #define BSK_ROPE_ABSOLUTE 2  /* key position = token index                     */
 
-#define BSK_TILE_DECODE 16   /* query-row tile of bsk_run_decode                 */
-#define BSK_TILE_PREFILL 128 /* query-row tile of bsk_run_prefill                */
+#define BSK_TILE_DECODE 16       /* query-row tile of bsk_run_decode             */
+#define BSK_TILE_PREFILL 128     /* query-row tiles of bsk_run_prefill: 32 rows  */
+#define BSK_TILE_PREFILL_256 256 /* per wave (two workgroups per CU) or 64 rows  */
+                                 /* per wave (one workgroup per CU)             */
 
 /*
  * Problem description shared by plan, run and merge.  Query rows of a
@@ -94,7 +96,7 @@ typedef struct bsk_problem {
   double rope_theta;     /* RoPE base                                          */
   float sm_scale;        /* logit scale, e.g. 1/sqrt(head_dim)                 */
   /* plan parameters (see bsk_plan) */
-  int32_t tile_q;        /* BSK_TILE_DECODE or BSK_TILE_PREFILL                */
+  int32_t tile_q;        /* BSK_TILE_DECODE, BSK_TILE_PREFILL or _PREFILL_256  */
   int32_t tile_kv;       /* chunk alignment, multiple of page_size             */
   int32_t num_workers;   /* persistent workgroups = launch grid (> 0)          */
   int32_t split_factor;  /* target chunks per worker (>= 1)                    */
@@ -228,12 +230,13 @@ bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info,
                           void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);
 
 /*
- * Large-tile attention (128 query rows per item): ragged (causal) prefill,
- * including prefill appended after cached KV ([FI-0.6, kernel types:
- * Prefill]) and the dense shared prefix of the composable format
- * ([FI-paper, methodology 1]).  bf16 only; QK^T and PV on bf16 MFMA with
- * fp32 accumulation.  Same output / partial-state contract as
- * bsk_run_decode.  Errors as bsk_run_decode (no RoPE).
+ * Large-tile attention (tile_q = 128 or 256 query rows per item): ragged
+ * (causal) prefill, including prefill appended after cached KV ([FI-0.6,
+ * kernel types: Prefill]) and the dense shared prefix of the composable
+ * format ([FI-paper, methodology 1]).  bf16 only; QK^T and PV on bf16 MFMA
+ * with fp32 accumulation.  Same output / partial-state contract as
+ * bsk_run_decode.  Errors as bsk_run_decode (no RoPE); also INVALID_ARG
+ * when a paged page stride exceeds 2^31 - 1 elements.
  */
 bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                            void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream);

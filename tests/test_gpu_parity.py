@@ -168,7 +168,7 @@ def test_determinism_and_page_permutation():
     compare(b1, O1, L1)
 
 
-@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL])
+@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL, bsk.TILE_PREFILL_256])
 def test_fused_merge_matches_separate_merge(tile_q):
     """In-kernel merge by the last chunk of each split unit gives exactly the
     separate merge kernel's result, leaves the arrival counters at zero, and a
@@ -191,33 +191,53 @@ def test_fused_merge_matches_separate_merge(tile_q):
     assert np.array_equal(out.double().cpu().numpy(), O2) and np.array_equal(lse.double().cpu().numpy(), L2)
 
 
-# ------------------------------------------------------------------ prefill (128-row tiles)
+# ------------------------------------------------------------------ prefill (128- and 256-row tiles)
 
-def test_prefill_small_several_tiles():
+PREFILL_TILES = [bsk.TILE_PREFILL, bsk.TILE_PREFILL_256]
+
+
+@pytest.mark.parametrize("tile_q", PREFILL_TILES)
+def test_prefill_small_several_tiles(tile_q):
     kv = np.array([300, 129, 77, 1000])
     qo = np.array([300, 40, 77, 130])
     b = small(60, kv, qo=qo, Hq=8, Hk=2, d=128, causal=True)
     for W_ in (5, 64):
-        O, L, _, _ = run(b, tile_q=bsk.TILE_PREFILL, num_workers=W_, split_factor=2, min_chunk=64)
+        say(f"prefill tile_q={tile_q} W={W_}")
+        O, L, _, _ = run(b, tile_q=tile_q, num_workers=W_, split_factor=2, min_chunk=64)
         compare(b, O, L)
 
 
-def test_prefill_head_dim_64_noncausal_and_window():
+@pytest.mark.parametrize("tile_q", PREFILL_TILES)
+def test_prefill_head_dim_64_noncausal_and_window(tile_q):
     kv = np.array([257, 64])
     b = small(61, kv, qo=np.array([100, 64]), Hq=4, Hk=4, d=64, causal=False)
-    O, L, _, _ = run(b, tile_q=bsk.TILE_PREFILL, num_workers=9, min_chunk=64)
+    O, L, _, _ = run(b, tile_q=tile_q, num_workers=9, min_chunk=64)
     compare(b, O, L)
     b2 = small(62, kv, qo=np.array([100, 64]), Hq=8, Hk=2, d=128, causal=True, window=50, sink=3)
-    O, L, _, _ = run(b2, tile_q=bsk.TILE_PREFILL, num_workers=9, min_chunk=64)
+    O, L, _, _ = run(b2, tile_q=tile_q, num_workers=9, min_chunk=64)
     compare(b2, O, L)
 
 
-def test_ragged_prefill_full_sampled():
+@pytest.mark.parametrize("tile_q", PREFILL_TILES)
+@pytest.mark.parametrize("ps,d", [(1, 128), (8, 64), (32, 128), (64, 128), (128, 128), (256, 64)])
+def test_prefill_page_sizes(tile_q, ps, d):
+    """Page sizes below, at and above the 64-key tile: the per-tile page slot / in-page offset
+    arithmetic of full tiles and the clamped ragged tail."""
+    kv = np.array([700, 64, 333, 1])
+    qo = np.array([200, 64, 333, 1])
+    b = small(63 + ps, kv, qo=qo, Hq=8, Hk=2, d=d, ps=ps, causal=True)
+    say(f"prefill tile_q={tile_q} page_size={ps} d={d}")
+    O, L, _, _ = run(b, tile_q=tile_q, num_workers=11, min_chunk=max(64, ps), tile_kv=max(64, ps))
+    compare(b, O, L)
+
+
+@pytest.mark.parametrize("tile_q", PREFILL_TILES)
+def test_ragged_prefill_full_sampled(tile_q):
     """16 requests, new lengths lognormal [128, 4096] appended after [0, 2048] cached keys,
     the benchmarked launch; checked on sampled query tokens (first, last, random)."""
     b = W.ragged_prefill()
-    say(f"ragged prefill: {int(b.qo_indptr[-1])} query tokens")
-    O, L, attn, _ = run(b, tile_q=bsk.TILE_PREFILL)
+    say(f"ragged prefill tile_q={tile_q}: {int(b.qo_indptr[-1])} query tokens")
+    O, L, attn, _ = run(b, tile_q=tile_q)
     rng = np.random.default_rng(0)
     toks = set()
     for r in range(b.batch_size):
@@ -229,10 +249,10 @@ def test_ragged_prefill_full_sampled():
 
 # ------------------------------------------------------------------ composable (dense prefix + paged suffix)
 
-def run_composable(c, prefix_workers=None, suffix_workers=None):
+def run_composable(c, prefix_workers=None, suffix_workers=None, prefix_tile=bsk.TILE_PREFILL):
     dev = require_gpu()
     pre, suf = c.prefix, c.suffix
-    Op, Lp, _, _ = run(pre, tile_q=bsk.TILE_PREFILL, num_workers=prefix_workers)
+    Op, Lp, _, _ = run(pre, tile_q=prefix_tile, num_workers=prefix_workers)
     Os, Ls, _, _ = run(suf, num_workers=suffix_workers)
     T, Hq, d = suf.q.shape
     oa = torch.from_numpy(Op.astype(np.float32)).to(dev)
@@ -246,10 +266,12 @@ def run_composable(c, prefix_workers=None, suffix_workers=None):
     return oo.double().cpu().numpy(), lo.double().cpu().numpy()
 
 
-def test_shared_prefix_composable_full():
+@pytest.mark.parametrize("prefix_tile", PREFILL_TILES)
+def test_shared_prefix_composable_full(prefix_tile):
     """16384-token dense prefix + 64 paged suffixes [128, 1024], merged by LSE."""
     c = W.shared_prefix()
-    O, L = run_composable(c)
+    say(f"composable prefix tile_q={prefix_tile}")
+    O, L = run_composable(c, prefix_tile=prefix_tile)
     pre, suf = c.prefix, c.suffix
     from oracle.attention import DenseKV
     kp, vp = suf.physical_pools()

@@ -121,7 +121,7 @@ def test_random_plans(seed):
     qo = np.minimum(kv, rng.choice([0, 1, 1, 3, 17, 200], size=B))
     Hk = int(rng.choice([1, 2, 8]))
     g = int(rng.choice([1, 4, 8]))
-    tile_q = int(rng.choice([bsk.TILE_DECODE, bsk.TILE_PREFILL]))
+    tile_q = int(rng.choice([bsk.TILE_DECODE, bsk.TILE_PREFILL, bsk.TILE_PREFILL_256]))
     window = int(rng.choice([0, 0, 5, 64, 1000]))
     tile_kv = int(rng.choice([16, 32, 64]))
     p = decode_problem(Hk * g, Hk, 64, int(rng.integers(1, 70)), tile_q=tile_q, causal=bool(rng.integers(0, 2)),
