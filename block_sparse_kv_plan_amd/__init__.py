@@ -13,6 +13,12 @@ import os
 
 import numpy as np
 
+# torch ships its own HIP/HSA runtime under the same sonames as /opt/rocm's.  Importing it first
+# makes libbsk's libamdhip64.so.7 / libhsa-runtime64.so.1 resolve to those already-loaded copies,
+# so the process holds one runtime and torch tensors and libbsk kernels share the device.  Loading
+# libbsk first would bring in a second runtime that does not see the device torch has opened.
+import torch  # noqa: F401  (load order only)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsk.so")
 if not os.path.exists(LIB_PATH):

@@ -10,16 +10,19 @@
 // Per item (request r, kv head h, rows [row_lo, row_lo + 64 NB), keys
 // [kv_lo, kv_hi)): each of the four waves owns 16 NB rows (NB 16-row MFMA
 // column blocks) and the whole key range.  Keys go through LDS in 64-key
-// tiles, double-buffered: the next tile's rows are fetched into registers
-// with coalesced 16-byte loads while the current tile is consumed, then
-// stored to the other buffer, so one barrier per tile suffices.
+// tiles, double-buffered, loaded by direct global-to-LDS transfers
+// (global_load_lds_dwordx4: every lane moves 16 bytes, a wave fills 1 KB
+// of LDS, no registers involved); the next tile's transfers are issued right
+// after the barrier that opens the current tile, so one barrier per tile
+// suffices.  LDS rows are unpadded; their 16-byte chunks are XOR-swizzled
+// by row so that both read patterns below are free of bank conflicts.
 //   S^T (64 x 16 NB) = K Q^T    16x16x32 bf16 MFMA, K from LDS, q in registers
 //   online softmax in base 2, fp32; masks are evaluated only on tiles that
 //   cross a boundary (range end, causal diagonal, window); the accumulator
 //   is rescaled only when a row's max grows by more than 2^8
-//   O^T (D x 16 NB) += V^T P^T  16x16x32 bf16 MFMA; each lane reads whole
-//   16-byte pieces of eight V rows and repacks them, the MFMA key index
-//   being mapped to the keys whose probabilities the lane already holds
+//   O^T (D x 16 NB) += V^T P^T  16x16x32 bf16 MFMA; V^T comes from
+//   transposing LDS reads, the MFMA key index being mapped to the keys
+//   whose probabilities the lane already holds
 // and every wave writes its own rows (output or partial state).
 //
 // Every K/V tile read from LDS is shared by all NB row blocks of a wave, so
@@ -41,6 +44,43 @@ constexpr int kPreThreads = kPreWaves * kWave;
 constexpr int kPreKeys = 64;                  // keys per LDS tile
 constexpr float kPreRescaleSlack = 8.f;       // log2 units
 
+// LDS byte address of a shared-memory location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// Direct global-to-LDS transfer of 16 bytes per lane: lane l's 16 bytes at g land at LDS byte
+// lds + 16 l (lds wave-uniform).  Completion is tracked by vmcnt only; the caller waits before
+// the barrier that publishes the tile.  Nothing else in these kernels relies on m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained) as a real instruction the compiler's wait
+// bookkeeping sees: after it no vector-memory load of this wave is outstanding, so the compiler
+// places no further vmcnt wait in front of uses of earlier loads (which would also stall on the
+// next tile's transfers).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_dma() {
+  asm volatile("" ::: "memory");
+  wait_vm();
+}
+
+// XOR swizzles of the 16-byte chunks of an LDS row.  K rows are read by 16 lanes at a time,
+// rows n = 0..15 at one logical chunk; V rows by the transposing reads, 4 rows x 2 chunks x 2
+// halves per 16 lanes and two such groups at a time.  Both patterns hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((2 * (r & 3)) ^ (8 * ((r >> 2) & 1))) : (2 * ((r >> 1) & 3));
+}
+
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
@@ -57,31 +97,26 @@ template <int D, bool DENSE, int NB>
 __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(AttnArgs a) {
   constexpr int ROWS = kPreWaves * 16 * NB;  // query rows per item (the plan's tile_q)
   constexpr int WROWS = 16 * NB;             // rows per wave
-  constexpr int ROW = D + 8;                 // bf16 per K row in LDS (padding spreads banks for
-                                             // the 16-byte row reads)
-  constexpr int ROWV = D + 16;               // bf16 per V row (spreads banks for the transposing reads)
   constexpr int NDB = D / 16;                // 16-column blocks of the output
   constexpr int NKS = D / 32;                // k-steps over d for the logits
-  constexpr int CHUNKS = D / 8;              // 16-byte pieces per row
-  constexpr int KPP = kPreThreads / CHUNKS;  // key rows per load pass
-  constexpr int NPASS = kPreKeys / KPP;      // load passes per tile
-  constexpr int TILE_ELEMS = kPreKeys * ROW;
-  constexpr int TILE_ELEMS_V = kPreKeys * ROWV;
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int RPW = kWave / CH;            // key rows one wave-wide transfer fills (1 KB)
+  constexpr int NP = kPreKeys / (kPreWaves * RPW);  // transfers per wave per tile and tensor
+  constexpr int TILE = kPreKeys * D;         // bf16 per LDS tile
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(NB == 2 || NB == 4, "row blocks per wave");
 
-  __shared__ __align__(16) unsigned short s_k[2 * TILE_ELEMS];
-  __shared__ __align__(16) unsigned short s_v[2 * TILE_ELEMS_V];
+  __shared__ __align__(1024) unsigned short s_k[2 * TILE];
+  __shared__ __align__(1024) unsigned short s_v[2 * TILE];
   __shared__ int32_t s_pages[DENSE ? 1 : kMaxPages];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int n = lane & 15;
   const int j = lane >> 4;
-  const int lc = tid % CHUNKS;  // load assignment: piece of a key row
-  const int lk = tid / CHUNKS;  // and the key row (plus multiples of KPP)
 
   const int32_t* __restrict__ ws = a.ws;
   const int it_begin = ws[HDR_WORDS + blockIdx.x];
@@ -98,6 +133,24 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
   // page strides in bytes; the host checks that they fit 32 bits
   const uint32_t k_page_bytes = uint32_t(a.k_sp) * 2u;
   const uint32_t v_page_bytes = uint32_t(a.v_sp) * 2u;
+  const uint32_t lds_k = lds_addr(s_k), lds_v = lds_addr(s_v);
+
+  // Transfer p of this wave fills tile rows (p * 4 + wave) * RPW .. + RPW - 1; lane l carries
+  // physical chunk l % CH of row (p * 4 + wave) * RPW + l / CH, i.e. the logical chunk that the
+  // row's swizzle maps there.
+  int trow[NP], ck[NP], cv[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    trow[p] = (p * kPreWaves + wave) * RPW + lane / CH;
+    ck[p] = (lane % CH) ^ swz_k<D>(trow[p]);
+    cv[p] = (lane % CH) ^ swz_v<D>(trow[p]);
+  }
+  // LDS read offsets (elements) that do not change from tile to tile
+  const int k_rd = n * D + 8 * 0;  // row n of each 16-key block; chunk added per k-step
+  const int k_sw = swz_k<D>(n);    // swizzle of rows 16 mb + n
+  const int v_row = 4 * j + (n >> 2);
+  const int v_sw = swz_v<D>(v_row);  // same for rows v_row + 16 i
+  const int v_half = 4 * (n & 1);
 
   for (int it = it_begin; it < it_end; ++it) {
     const int32_t* rec = items + int64_t(it) * ITEM_WORDS;
@@ -110,6 +163,7 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
     const int L = kv_lens[r];
     const int kbase = kv_ind[r];
 
+    __syncthreads();  // the previous item is done with the page list and the tiles
     if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, kPreThreads);
     __syncthreads();
 
@@ -147,78 +201,70 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
       for (int db = 0; db < NDB; ++db) acc[nb][db] = f32x4{0, 0, 0, 0};
     }
 
-    // Load addressing.  Thread (lk, lc) fetches piece lc of key rows lk + p KPP of each tile.
-    // When tiles start at multiples of 64 keys (always for dense KV; for paged KV when the item
-    // does), a full tile's row p sits in page slot (kt >> shift) - p0 + slot_p at in-page token
-    // (kt & pmask) + (r_p & pmask): a page of <= 64 keys divides the tile, a larger page holds all
-    // of it.  Then the address is one 32 x 32 -> 64-bit multiply-add of the page id.
+    // Transfer addressing.  When tiles start at multiples of 64 keys (always for dense KV; for
+    // paged KV when the item does), a full tile's row t sits in page slot (kt >> shift) - p0 +
+    // (t >> shift) at in-page token (kt & pmask) + (t & pmask): a page of <= 64 keys divides the
+    // tile, a larger page holds all of it.  The 32-bit per-row part (head, in-page or in-tile
+    // token, chunk) is below the page stride (paged) or 2^31 (dense, checked by the host).
     const bool fast_item = DENSE || (kv_lo & (kPreKeys - 1)) == 0;
-    // 32-bit part of each row's address that does not change from tile to tile: head, in-page
-    // token (paged) or tile-relative token (dense), and the 16-byte piece.  It is below the page
-    // stride (paged) or below 2^32 for dense blocks the host accepts.
-    uint32_t koff[NPASS], voff[NPASS];
+    uint32_t koff[NP], voff[NP];
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const int rr = lk + p * KPP;
-      const int tok = DENSE ? rr : (rr & pmask);
-      koff[p] = uint32_t(2 * (int64_t(h) * a.k_sh + int64_t(tok) * a.k_st + 8 * lc));
-      voff[p] = uint32_t(2 * (int64_t(h) * a.v_sh + int64_t(tok) * a.v_st + 8 * lc));
+    for (int p = 0; p < NP; ++p) {
+      const int tok = DENSE ? trow[p] : (trow[p] & pmask);
+      koff[p] = uint32_t(2 * (int64_t(h) * a.k_sh + int64_t(tok) * a.k_st) + 16 * ck[p]);
+      voff[p] = uint32_t(2 * (int64_t(h) * a.v_sh + int64_t(tok) * a.v_st) + 16 * cv[p]);
     }
     const int p0 = kv_lo >> a.page_shift;
 
-    bf16x8 kreg[NPASS], vreg[NPASS];
-    auto load_tile = [&](int kt) {
+    auto load_tile = [&](int kt, int buf) {
+      const uint32_t lk0 = lds_k + uint32_t(buf * TILE * 2), lv0 = lds_v + uint32_t(buf * TILE * 2);
       if (fast_item && kt + kPreKeys <= kv_hi) {
         if constexpr (DENSE) {
           const char* kb = reinterpret_cast<const char*>(Kp) + 2 * (int64_t(kbase + kt) * a.k_st);
           const char* vb = reinterpret_cast<const char*>(Vp) + 2 * (int64_t(kbase + kt) * a.v_st);
 #pragma unroll
-          for (int p = 0; p < NPASS; ++p) {
-            kreg[p] = *reinterpret_cast<const bf16x8*>(kb + koff[p]);
-            vreg[p] = *reinterpret_cast<const bf16x8*>(vb + voff[p]);
+          for (int p = 0; p < NP; ++p) {
+            const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+            dma16(kb + koff[p], lk0 + lo);
+            dma16(vb + voff[p], lv0 + lo);
           }
         } else {
           const int sb = (kt >> a.page_shift) - p0;
           const char* kb = reinterpret_cast<const char*>(Kp) + 2 * (int64_t(kt & pmask) * a.k_st);
           const char* vb = reinterpret_cast<const char*>(Vp) + 2 * (int64_t(kt & pmask) * a.v_st);
 #pragma unroll
-          for (int p = 0; p < NPASS; ++p) {
-            const uint32_t page = uint32_t(s_pages[sb + ((lk + p * KPP) >> a.page_shift)]);
-            kreg[p] = *reinterpret_cast<const bf16x8*>(kb + (uint64_t(page) * k_page_bytes + koff[p]));
-            vreg[p] = *reinterpret_cast<const bf16x8*>(vb + (uint64_t(page) * v_page_bytes + voff[p]));
+          for (int p = 0; p < NP; ++p) {
+            const uint32_t page = uint32_t(s_pages[sb + (trow[p] >> a.page_shift)]);
+            const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+            dma16(kb + (uint64_t(page) * k_page_bytes + koff[p]), lk0 + lo);
+            dma16(vb + (uint64_t(page) * v_page_bytes + voff[p]), lv0 + lo);
           }
         }
       } else {
-        // ragged tail or unaligned start: clamp rows past the range to the last key
+        // ragged tail or unaligned start: rows past the range repeat the last key (masked later)
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-          const int t = min(kt + lk + p * KPP, kv_hi - 1);
+        for (int p = 0; p < NP; ++p) {
+          const int t = min(kt + trow[p], kv_hi - 1);
           const int64_t ko = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
           const int64_t vo = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
-          kreg[p] = *reinterpret_cast<const bf16x8*>(Kp + ko + 8 * lc);
-          vreg[p] = *reinterpret_cast<const bf16x8*>(Vp + vo + 8 * lc);
+          const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+          dma16(Kp + ko + 8 * ck[p], lk0 + lo);
+          dma16(Vp + vo + 8 * cv[p], lv0 + lo);
         }
       }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        *reinterpret_cast<bf16x8*>(s_k + buf * TILE_ELEMS + (lk + p * KPP) * ROW + 8 * lc) = kreg[p];
-        *reinterpret_cast<bf16x8*>(s_v + buf * TILE_ELEMS_V + (lk + p * KPP) * ROWV + 8 * lc) = vreg[p];
-      }
-    };
 
-    const int ntiles = (kv_hi - kv_lo + kPreKeys - 1) / kPreKeys;
-    load_tile(kv_lo);
-    store_tile(0);
-    __syncthreads();
+    const int ntiles = (kv_hi - kv_lo + kPreKeys - 1) / kPreKeys;  // items are never empty
+    wait_vm();  // q fragments and page ids are in registers before the tile loop starts
+    if (ntiles > 0) load_tile(kv_lo, 0);
     for (int tile = 0; tile < ntiles; ++tile) {
       const int kt = kv_lo + tile * kPreKeys;
       const int buf = tile & 1;
-      const bool more = tile + 1 < ntiles;
-      if (more) load_tile(kt + kPreKeys);  // in flight during this tile's math
-      const unsigned short* sk = s_k + buf * TILE_ELEMS;
-      const unsigned short* sv = s_v + buf * TILE_ELEMS_V;
+      wait_dma();        // this wave's transfers of the tile have landed
+      __syncthreads();   // ... and every other wave's; the other buffer is free again
+      if (tile + 1 < ntiles) load_tile(kt + kPreKeys, buf ^ 1);  // in flight during this tile's math
+      const unsigned short* sk = s_k + buf * TILE;
+      const unsigned short* sv = s_v + buf * TILE;
 
       if (wave_has_rows) {
         // masks only where the tile crosses a boundary for some row of this wave
@@ -226,26 +272,41 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
         bool clean = all_rows && kend < kv_hi;
         if (a.causal) clean = clean && kend <= wq_lo;
         if (a.window > 0) clean = clean && (wq_hi - kt) < a.window;
-        // two 32-key halves, each: logits, softmax, PV (halves the live logit registers)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          // S^T[key][row] for key blocks 2ks, 2ks+1 x NB row blocks
-          f32x4 st[2][NB];
+        // Logits of a 32-key half: all its K fragments are read first (their LDS latencies
+        // overlap), then the MFMAs.
+        auto logits = [&](int ks, f32x4 (&st)[2][NB]) {
 #pragma unroll
           for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) st[mh][nb] = f32x4{0, 0, 0, 0};
+          bf16x8 kf[2][NKS];
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) {
+          for (int s = 0; s < NKS; ++s)
 #pragma unroll
-            for (int mh = 0; mh < 2; ++mh) {
-              const int mb = 2 * ks + mh;
-              const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + (16 * mb + n) * ROW + 8 * (4 * s + j));
+            for (int mh = 0; mh < 2; ++mh)
+              kf[mh][s] = *reinterpret_cast<const bf16x8*>(sk + 16 * (2 * ks + mh) * D + k_rd +
+                                                           8 * ((4 * s + j) ^ k_sw));
+#pragma unroll
+          for (int s = 0; s < NKS; ++s)
+#pragma unroll
+            for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb)
-                st[mh][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nb][s], st[mh][nb], 0, 0, 0);
-            }
-          }
+                st[mh][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mh][s], qf[nb][s], st[mh][nb], 0, 0, 0);
+        };
+        // With two row blocks the logits of both halves are issued first: each half's softmax then
+        // runs on the VALU while the matrix cores still work on the other half's logits (or the
+        // previous PV).  With four row blocks the registers allow only one half at a time.
+        constexpr int LIVE = NB <= 2 ? 2 : 1;
+        f32x4 st2[LIVE][2][NB];
+        if constexpr (LIVE == 2) {
+          logits(0, st2[0]);
+          logits(1, st2[1]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if constexpr (LIVE == 1) logits(ks, st2[0]);
+          f32x4 (&st)[2][NB] = st2[LIVE == 2 ? ks : 0];
           if (!clean) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -308,19 +369,25 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
           // LDS reads: in each 16-lane group, lane k points at 4 columns of key row k/4 and gets
           // back one column of 4 keys, so lane (n, j) receives V[key(8j+e)][16 db + n].
           {
-            const unsigned short* vb = sv + (32 * ks + 4 * j + (n >> 2)) * ROWV + 4 * (n & 3);
+            const unsigned short* vb = sv + (32 * ks + v_row) * D + v_half;
+            constexpr int VB = NB <= 2 ? NDB : 2;  // V^T operands read ahead of their MFMAs
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const bf16x8 va = ds_read_tr_pair(vb + 16 * db, vb + 16 * db + 16 * ROWV);
+            for (int d0 = 0; d0 < NDB; d0 += VB) {
+              bf16x8 va[VB];
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[nb], acc[nb][db], 0, 0, 0);
+              for (int i = 0; i < VB; ++i) {
+                const int off = 8 * ((2 * (d0 + i) + ((n & 3) >> 1)) ^ v_sw);
+                va[i] = ds_read_tr_pair(vb + off, vb + off + 16 * D);
+              }
+#pragma unroll
+              for (int i = 0; i < VB; ++i)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                  acc[nb][d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pb[nb], acc[nb][d0 + i], 0, 0, 0);
             }
           }
         }
       }
-      if (more) store_tile(buf ^ 1);  // the other buffer was last read before the previous barrier
-      __syncthreads();
     }
 
     // epilogue: each lane owns row n of each row block and columns 16 db + 4 j .. + 3
