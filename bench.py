@@ -90,14 +90,14 @@ def make_attention(batch, tile_q, out_dtype, device, **kw):
 class Runner:
     """Device copies of one batch plus two alternating plan workspaces."""
 
-    def __init__(self, batch, tile_q, copies, device, out_dtype=0):
+    def __init__(self, batch, tile_q, copies, device, out_dtype=0, **plan_kw):
         import torch
 
         import block_sparse_kv_plan_amd as bsk
         from block_sparse_kv_plan_amd.attention import tensors_for
         from tests.gpu_util import rope_positions_needed, upload
         self.batch = batch
-        self.attn = [make_attention(batch, tile_q, out_dtype, device) for _ in range(2)]
+        self.attn = [make_attention(batch, tile_q, out_dtype, device, **plan_kw) for _ in range(2)]
         T = int(batch.qo_indptr[-1])
         o_dt = torch.bfloat16 if out_dtype == bsk.DTYPE_BF16 else torch.float32
         self.out = torch.zeros((T, batch.num_qo_heads, batch.head_dim), dtype=o_dt, device=device)
@@ -211,6 +211,9 @@ def main():
     ap.add_argument("--only", default="", help="profiling aid: run just this workload (decode|prefill|composable|rope)")
     ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
                     help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
+    ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
+    ap.add_argument("--decode-min-chunk", type=int, default=None, help="plan min_chunk (keys) of the decode workload")
+    ap.add_argument("--decode-overhead", type=int, default=None, help="plan item_overhead (keys) of the decode workload")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
@@ -242,7 +245,9 @@ def main():
         log("decode: generating the Llama-3-8B-shaped batch")
         b = W.llama3_decode()
         nbytes = decode_bytes(b)
-        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device)
+        dkw = {k: v for k, v in (("split_factor", args.decode_split), ("min_chunk", args.decode_min_chunk),
+                                  ("item_overhead", args.decode_overhead)) if v is not None}
+        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device, **dkw)
         log(f"decode: {int(b.kv_len.sum())} keys, {nbytes / 1e9:.3f} GB per step; timing {args.steps} steps")
         m = timed(runner, args.steps, args.warmup)
         info = runner.attn[0].info

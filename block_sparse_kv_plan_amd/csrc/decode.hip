@@ -129,9 +129,6 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
   const int it_begin = ws[HDR_WORDS + blockIdx.x];
   const int it_end = ws[HDR_WORDS + blockIdx.x + 1];
   const int32_t* __restrict__ items = ws + ws[HDR_OFF_ITEMS];
-  const int32_t* __restrict__ qo_indptr = ws + ws[HDR_OFF_QO];
-  const int32_t* __restrict__ kv_lens = ws + ws[HDR_OFF_KVLEN];
-  const int32_t* __restrict__ kv_ind = ws + ws[HDR_OFF_KVIND];
   const T* __restrict__ Qp = static_cast<const T*>(a.q);
   const T* __restrict__ Kp = static_cast<const T*>(a.k);
   const T* __restrict__ Vp = static_cast<const T*>(a.v);
@@ -144,10 +141,11 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
     const int row_lo = rec[IT_ROW_LO], row_hi = rec[IT_ROW_HI];
     const int kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI];
     const int slot = rec[IT_SLOT];
-    const int q0 = qo_indptr[r];
-    const int qlen = qo_indptr[r + 1] - q0;
-    const int L = kv_lens[r];
-    const int kbase = kv_ind[r];
+    const int q0 = rec[IT_Q0];
+    const int qlen = rec[IT_QLEN];
+    const int L = rec[IT_KVLEN];
+    const int kbase = rec[IT_KBASE];
+    (void)r;
 
     if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, kDecThreads);
     __syncthreads();

@@ -172,6 +172,35 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
 
 namespace bsk {
 
+// LDS byte address of a shared-memory location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// Direct global-to-LDS transfers: lane l's 16 (4) bytes at g land at LDS byte lds + 16 l
+// (lds + 4 l), lds wave-uniform.  Written as inline assembly so that the compiler adds no waits
+// of its own; completion is tracked by vmcnt only and the caller waits (wait_vm) before the
+// barrier that publishes the data.  Nothing else in these kernels relies on m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained) as a real instruction the compiler's wait
+// bookkeeping sees: after it no vector-memory load of this wave is outstanding, so the compiler
+// places no further vmcnt wait in front of uses of earlier loads (which would also stall on the
+// next tile's transfers).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_dma() {
+  asm volatile("" ::: "memory");
+  wait_vm();
+}
+
 // Block-sparse gather, part 1: stage the page ids an item needs -- pages
 // kv_lo / page_size .. (kv_hi - 1) / page_size of request r's page list --
 // into LDS, so every later key address is one LDS read away.  All threads

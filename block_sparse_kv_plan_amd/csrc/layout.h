@@ -42,7 +42,7 @@ enum : int {
   HDR_WORDS = 16,
 };
 
-// item record
+// item record (64 bytes: one scalar load brings everything a worker needs to start the item)
 enum : int {
   IT_R = 0,       // request
   IT_H = 1,       // kv head
@@ -52,7 +52,11 @@ enum : int {
   IT_KV_HI = 5,   // one past the last key
   IT_SLOT = 6,    // partial-state slot, or -1: write the output directly
   IT_ID = 7,      // creation index
-  ITEM_WORDS = 8,
+  IT_Q0 = 8,      // the request's qo_indptr[r]: its first query token
+  IT_QLEN = 9,    // the request's query length
+  IT_KVLEN = 10,  // the request's kv_len
+  IT_KBASE = 11,  // the request's kv_indptr[r]: first page (paged) or token (dense) offset
+  ITEM_WORDS = 16,  // words 12..15 are zero
 };
 
 // merge record

@@ -98,13 +98,12 @@ __global__ __launch_bounds__(256) void gather_kernel(AttnArgs a, const int64_t* 
   const int it_begin = ws[HDR_WORDS + blockIdx.x];
   const int it_end = ws[HDR_WORDS + blockIdx.x + 1];
   const int32_t* __restrict__ items = ws + ws[HDR_OFF_ITEMS];
-  const int32_t* __restrict__ kv_ind = ws + ws[HDR_OFF_KVIND];
   const T* K = static_cast<const T*>(a.k);
   const T* V = static_cast<const T*>(a.v);
   for (int it = it_begin; it < it_end; ++it) {
     const int32_t* rec = items + int64_t(it) * ITEM_WORDS;
-    const int r = rec[IT_R], h = rec[IT_H], kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI], id = rec[IT_ID];
-    const int kbase = kv_ind[r];
+    const int h = rec[IT_H], kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI], id = rec[IT_ID];
+    const int kbase = rec[IT_KBASE];
     if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, threadIdx.x, 256);
     __syncthreads();
     const int64_t base = row_off[id];

@@ -312,6 +312,10 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     rec[IT_KV_HI] = it.kv_hi;
     rec[IT_SLOT] = it.slot;
     rec[IT_ID] = id;
+    rec[IT_Q0] = qo_indptr[it.r];
+    rec[IT_QLEN] = qo_indptr[it.r + 1] - qo_indptr[it.r];
+    rec[IT_KVLEN] = kv_len[it.r];
+    rec[IT_KBASE] = kv_indptr[it.r];
   }
   for (size_t m = 0; m < merges.size(); ++m) {
     int32_t* rec = buf + L.off_merge + int64_t(m) * MERGE_WORDS;

@@ -44,31 +44,6 @@ constexpr int kPreThreads = kPreWaves * kWave;
 constexpr int kPreKeys = 64;                  // keys per LDS tile
 constexpr float kPreRescaleSlack = 8.f;       // log2 units
 
-// LDS byte address of a shared-memory location.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
-}
-
-// Direct global-to-LDS transfer of 16 bytes per lane: lane l's 16 bytes at g land at LDS byte
-// lds + 16 l (lds wave-uniform).  Completion is tracked by vmcnt only; the caller waits before
-// the barrier that publishes the tile.  Nothing else in these kernels relies on m0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained) as a real instruction the compiler's wait
-// bookkeeping sees: after it no vector-memory load of this wave is outstanding, so the compiler
-// places no further vmcnt wait in front of uses of earlier loads (which would also stall on the
-// next tile's transfers).
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ __forceinline__ void wait_dma() {
-  asm volatile("" ::: "memory");
-  wait_vm();
-}
-
 // XOR swizzles of the 16-byte chunks of an LDS row.  K rows are read by 16 lanes at a time,
 // rows n = 0..15 at one logical chunk; V rows by the transposing reads, 4 rows x 2 chunks x 2
 // halves per 16 lanes and two such groups at a time.  Both patterns hit distinct banks.
@@ -122,9 +97,6 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
   const int it_begin = ws[HDR_WORDS + blockIdx.x];
   const int it_end = ws[HDR_WORDS + blockIdx.x + 1];
   const int32_t* __restrict__ items = ws + ws[HDR_OFF_ITEMS];
-  const int32_t* __restrict__ qo_indptr = ws + ws[HDR_OFF_QO];
-  const int32_t* __restrict__ kv_lens = ws + ws[HDR_OFF_KVLEN];
-  const int32_t* __restrict__ kv_ind = ws + ws[HDR_OFF_KVIND];
   const __bf16* __restrict__ Qp = static_cast<const __bf16*>(a.q);
   const __bf16* __restrict__ Kp = static_cast<const __bf16*>(a.k);
   const __bf16* __restrict__ Vp = static_cast<const __bf16*>(a.v);
@@ -158,10 +130,11 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
     const int row_lo = rec[IT_ROW_LO], row_hi = rec[IT_ROW_HI];
     const int kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI];
     const int slot = rec[IT_SLOT];
-    const int q0 = qo_indptr[r];
-    const int qlen = qo_indptr[r + 1] - q0;
-    const int L = kv_lens[r];
-    const int kbase = kv_ind[r];
+    const int q0 = rec[IT_Q0];
+    const int qlen = rec[IT_QLEN];
+    const int L = rec[IT_KVLEN];
+    const int kbase = rec[IT_KBASE];
+    (void)r;
 
     __syncthreads();  // the previous item is done with the page list and the tiles
     if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, kPreThreads);

@@ -60,6 +60,12 @@ def assert_same_plan(problem, qo_len, kv_len):
         want = np.concatenate([ref["items"][ids], np.asarray(ids, dtype=np.int64)[:, None]], axis=1) \
             if ids else np.zeros((0, 8), dtype=np.int64)
         assert np.array_equal(got["worker_items"][w].astype(np.int64), want), f"worker {w}"
+        # the record also carries its request's offsets and lengths, copied from the inputs
+        r = got["worker_items"][w][:, 0].astype(np.int64)
+        req = np.stack([qo_indptr[r], qo_indptr[r + 1] - qo_indptr[r], np.asarray(kv_len)[r], kv_indptr[r]], axis=1) \
+            if len(r) else np.zeros((0, 4), dtype=np.int64)
+        assert np.array_equal(got["worker_req"][w].astype(np.int64), req.astype(np.int64)), f"worker {w} request fields"
+    assert (got["item_pad"] == 0).all()
     assert np.array_equal(got["merge"][:, :6].astype(np.int64), ref["merge"])
     assert info.max_load == int(ref["load"].max()) if len(ref["items"]) else True
     assert np.array_equal(got["qo_indptr"], qo_indptr)
