@@ -425,3 +425,76 @@ def test_plan_tiny_decode_by_hand():
     assert spans[(3, 0)] == [(0, 64), (64, 128), (128, 192), (192, 255)]
     assert spans[(0, 0)] == [(0, 17)]
     assert plan["worker_items"] == [[2, 12], [3, 14], [4, 15], [5, 16], [7, 13], [8, 17], [10, 0, 6], [11, 1, 9]]
+
+
+# ------------------------------------------------------------------ append (chunked prefill)
+
+def _append_case(seed, layout="HND"):
+    rng = np.random.default_rng(seed)
+    ps, Hk, d = 4, 2, 8
+    P = np.array([5, 0, 8, 3])           # cached tokens before the append
+    n = np.array([3, 6, 0, 9])           # new tokens
+    after = P + n
+    pages = (after + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(pages)])
+    pool = int(indptr[-1]) + 3           # some pages belong to nobody
+    perm = rng.permutation(pool)[:int(indptr[-1])]
+    shape = (pool, Hk, ps, d) if layout == "HND" else (pool, ps, Hk, d)
+    k = rng.standard_normal(shape).astype(np.float32)
+    v = rng.standard_normal(shape).astype(np.float32)
+    app = np.concatenate([[0], np.cumsum(n)])
+    kn = rng.standard_normal((int(app[-1]), Hk, d)).astype(np.float32)
+    vn = rng.standard_normal((int(app[-1]), Hk, d)).astype(np.float32)
+    return dict(k=k, v=v, indptr=indptr, perm=perm, ps=ps, P=P, n=n, after=after, app=app, kn=kn, vn=vn,
+                layout=layout)
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_append_then_gather_is_prefix_plus_new(layout):
+    """Gathering the appended cache (through the separately pinned gather) gives the request's old
+    prefix followed by exactly its new tokens."""
+    c = _append_case(70, layout)
+    k2, v2 = oracle.append_paged_kv(c["k"], c["v"], c["indptr"], c["perm"], c["ps"], c["app"], c["after"],
+                                    c["kn"], c["vn"], layout=layout)
+    before = PagedKV(c["k"], c["v"], c["indptr"], c["perm"], c["ps"], layout)
+    after = PagedKV(k2, v2, c["indptr"], c["perm"], c["ps"], layout)
+    for r in range(len(c["P"])):
+        P, n = int(c["P"][r]), int(c["n"][r])
+        kb, vb = oracle.gather_kv(before, r, np.arange(P))
+        ka, va = oracle.gather_kv(after, r, np.arange(P + n))
+        a = int(c["app"][r])
+        assert np.array_equal(ka, np.concatenate([kb, c["kn"][a:a + n].astype(np.float64)]))
+        assert np.array_equal(va, np.concatenate([vb, c["vn"][a:a + n].astype(np.float64)]))
+
+
+def test_append_leaves_other_slots_untouched():
+    c = _append_case(71)
+    k2, v2 = oracle.append_paged_kv(c["k"], c["v"], c["indptr"], c["perm"], c["ps"], c["app"], c["after"],
+                                    c["kn"], c["vn"])
+    written = np.zeros(c["k"].shape[:1] + c["k"].shape[2:3], dtype=bool)  # [page, slot]
+    for r in range(len(c["P"])):
+        for pos in range(int(c["P"][r]), int(c["after"][r])):
+            written[int(c["perm"][int(c["indptr"][r]) + pos // c["ps"]]), pos % c["ps"]] = True
+    assert written.sum() == int(c["n"].sum())
+    keep = ~written
+    assert np.array_equal(k2.transpose(0, 2, 1, 3)[keep], c["k"].transpose(0, 2, 1, 3)[keep])
+    assert np.array_equal(v2.transpose(0, 2, 1, 3)[keep], c["v"].transpose(0, 2, 1, 3)[keep])
+
+
+def test_append_in_two_steps_equals_one():
+    """Appending a request's new tokens in two chunks (the chunked-prefill schedule) leaves the
+    same cache as appending them at once."""
+    c = _append_case(72)
+    one = oracle.append_paged_kv(c["k"], c["v"], c["indptr"], c["perm"], c["ps"], c["app"], c["after"],
+                                 c["kn"], c["vn"])
+    first = c["n"] // 2
+    second = c["n"] - first
+    idx1 = np.concatenate([np.arange(c["app"][r], c["app"][r] + first[r]) for r in range(len(c["n"]))])
+    idx2 = np.concatenate([np.arange(c["app"][r] + first[r], c["app"][r + 1]) for r in range(len(c["n"]))])
+    app1 = np.concatenate([[0], np.cumsum(first)])
+    app2 = np.concatenate([[0], np.cumsum(second)])
+    k1, v1 = oracle.append_paged_kv(c["k"], c["v"], c["indptr"], c["perm"], c["ps"], app1, c["P"] + first,
+                                    c["kn"][idx1.astype(int)], c["vn"][idx1.astype(int)])
+    k2, v2 = oracle.append_paged_kv(k1, v1, c["indptr"], c["perm"], c["ps"], app2, c["after"],
+                                    c["kn"][idx2.astype(int)], c["vn"][idx2.astype(int)])
+    assert np.array_equal(k2, one[0]) and np.array_equal(v2, one[1])
