@@ -208,7 +208,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="profiling aid: run just this workload (decode|prefill|composable|rope)")
+    ap.add_argument("--only", default="",
+                    help="profiling aid: run just this workload (decode|prefill|append|composable|rope)")
     ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
                     help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
     ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
@@ -302,6 +303,68 @@ def main():
             "unmasked_pairs": pairs, "flops": flops, "tile_q": args.prefill_tile,
             "num_workers": runner.attn[0].info.num_workers, "items": runner.attn[0].info.num_items}
         del runner
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "append"):
+        log("append: new tokens' K/V of the ragged prefill into the paged cache; chunked prefill")
+        from block_sparse_kv_plan_amd.attention import BatchAttention, chunked_prefill, pool_strides
+        from tests.gpu_util import upload
+        b = W.ragged_prefill()
+        du = upload(b, device=device)
+        new = b.qo_len.astype(np.int64)
+        prefix = b.kv_len.astype(np.int64) - new
+        T = int(new.sum())
+        el = 2
+        kn = torch.randn((T, b.num_kv_heads, b.head_dim), device=device).to(torch.bfloat16)
+        vn = torch.randn((T, b.num_kv_heads, b.head_dim), device=device).to(torch.bfloat16)
+        prob = make_attention(b, bsk.TILE_PREFILL, 0, device).problem
+        app = torch.as_tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32), device=device)
+        kvl = torch.as_tensor(b.kv_len.astype(np.int32), device=device)
+        pip = torch.as_tensor(du["kv_indptr"], device=device)
+        stream = torch.cuda.current_stream()
+
+        def do_append():
+            bsk.append_paged_kv(prob, b.batch_size, T, app, kvl, pip, du["pages"], kn, vn, kn.stride(0),
+                                kn.stride(1), du["k"], du["v"], pool_strides(du["k"]), pool_strides(du["v"]), stream)
+        for _ in range(3):
+            do_append()
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            do_append()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        app_s = e0.elapsed_time(e1) * 1e-3 / reps
+        app_bytes = 2 * 2 * T * b.num_kv_heads * b.head_dim * el  # K and V, read and written
+        secondary["append_paged_kv"] = {
+            "workload": f"the ragged prefill's {T} new tokens, 8 kv heads, d128, bf16, page 16",
+            "us": round(app_s * 1e6, 2), "gbs": round(app_bytes / app_s / 1e9, 1),
+            "frac_of_hbm_peak": round(app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 4), "bytes": app_bytes}
+        flops, _ = prefill_flops(b)
+        attn = BatchAttention.create(device=device, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
+                                     head_dim=b.head_dim, dtype=bsk.DTYPE_BF16, page_size=b.page_size, causal=True,
+                                     tile_q=args.prefill_tile, max_batch=b.batch_size)
+        out = torch.empty((T, b.num_qo_heads, b.head_dim), dtype=torch.float32, device=device)
+        lse = torch.empty((T, b.num_qo_heads), dtype=torch.float32, device=device)
+        chunk = 4096
+        chunked_prefill(attn, du["q"], kn, vn, out, lse, du["k"], du["v"], du["pages"], du["kv_indptr"], prefix,
+                        new, chunk)
+        torch.cuda.synchronize()
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            chunked_prefill(attn, du["q"], kn, vn, out, lse, du["k"], du["v"], du["pages"], du["kv_indptr"], prefix,
+                            new, chunk)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / reps
+        secondary["chunked_prefill"] = {
+            "workload": f"the ragged prefill run as steps of {chunk} new tokens (append + plan + prefill + merge "
+                        f"per step), tile_q {args.prefill_tile}",
+            "steps": (T + chunk - 1) // chunk, "wall_ms": round(wall * 1e3, 3),
+            "tflops_incl_host_steps": round(flops / wall / 1e12, 1)}
+        del attn, du
         torch.cuda.empty_cache()
 
     if not args.no_secondary and args.only in ("", "rope"):

@@ -74,6 +74,8 @@ _sig = {
     "bsk_merge_state_pair": [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp],
     "bsk_rope_table": [vp, i32, i32, f64, vp],
     "bsk_debug_gather": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp, vp, vp],
+    "bsk_append_paged_kv": [P(Problem), i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64,
+                            i64, vp],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).restype = i32
@@ -175,6 +177,16 @@ def merge_state_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows: int, head_dim
 
 def rope_table(table, n_pos: int, head_dim: int, theta: float, stream=None):
     _ok(_lib.bsk_rope_table(_ptr(table), n_pos, head_dim, float(theta), _stream(stream)))
+
+
+def append_paged_kv(problem: Problem, batch: int, n_total: int, append_indptr, kv_len, kv_page_indptr,
+                    kv_page_indices, k_new, v_new, new_stride_tok: int, new_stride_head: int, k_cache, v_cache,
+                    k_strides, v_strides, stream=None):
+    """k_strides / v_strides: (page, head, token) element strides of the pools."""
+    _ok(_lib.bsk_append_paged_kv(ctypes.byref(problem), batch, n_total, _ptr(append_indptr), _ptr(kv_len),
+                                 _ptr(kv_page_indptr), _ptr(kv_page_indices), _ptr(k_new), _ptr(v_new),
+                                 int(new_stride_tok), int(new_stride_head), _ptr(k_cache), _ptr(v_cache),
+                                 *(int(x) for x in k_strides), *(int(x) for x in v_strides), _stream(stream)))
 
 
 def debug_gather(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, row_offsets, k_out, v_out,

@@ -12,8 +12,8 @@ import numpy as np
 import torch
 
 from . import (DTYPE_BF16, DTYPE_F32, KV_DENSE, KV_PAGED, ROPE_NONE, TILE_DECODE, TILE_PREFILL, TILE_PREFILL_256, PlanInfo,
-               Problem, Tensors, device_workers, merge_state_pair, merge_states, plan, run_decode, run_prefill,
-               workspace_query)
+               Problem, Tensors, append_paged_kv, device_workers, merge_state_pair, merge_states, plan, run_decode,
+               run_prefill, workspace_query)
 
 TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
 
@@ -141,3 +141,51 @@ def merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
     out_dtype = DTYPE_BF16 if o_out.dtype == torch.bfloat16 else DTYPE_F32
     merge_state_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, d, out_dtype,
                      stream or torch.cuda.current_stream(o_a.device))
+
+
+def pool_strides(pool, layout="HND"):
+    """(page, head, token) element strides of a K or V pool tensor."""
+    if layout == "HND":
+        return pool.stride(0), pool.stride(1), pool.stride(2)
+    if layout == "NHD":
+        return pool.stride(0), pool.stride(2), pool.stride(1)
+    raise ValueError(layout)
+
+
+def chunked_prefill(attn: BatchAttention, q, k_new, v_new, out, lse, k_pool, v_pool, page_indices,
+                    kv_page_indptr, prefix_len, new_len, chunk_tokens: int, layout="HND", stream=None):
+    """Causal prefill of new tokens appended after cached ones, in steps of at most chunk_tokens
+    tokens (chunked prefill, FlashInfer 0.6 wiki "Kernel types": Prefill).
+
+    The new tokens are the rows of q / k_new / v_new, request after request (new_len[r] rows of
+    request r, whose first prefix_len[r] tokens are already in the cache).  Step s takes rows
+    [s * chunk_tokens, (s + 1) * chunk_tokens): each request contributes one contiguous run of its
+    tokens, so the step's q, K/V and output rows are views.  A step appends its rows' K/V to the
+    pages (bsk_append_paged_kv), plans the step with kv_len = cached + appended so far, and runs
+    the prefill kernel plus the merge; all device work is the library's.  attn must be a
+    prefill-class BatchAttention over the same problem; kv_page_indptr is a host array."""
+    stream = stream or torch.cuda.current_stream(attn.device)
+    prefix_len = np.asarray(prefix_len, dtype=np.int64)
+    new_len = np.asarray(new_len, dtype=np.int64)
+    starts = np.concatenate([[0], np.cumsum(new_len)])
+    n_total = int(starts[-1])
+    page_indptr_host = np.asarray(kv_page_indptr, dtype=np.int32)
+    page_indptr_dev = torch.as_tensor(page_indptr_host).to(attn.device)
+    ks, vs = pool_strides(k_pool, layout), pool_strides(v_pool, layout)
+    p = attn.problem
+    for c0 in range(0, n_total, chunk_tokens):
+        c1 = min(c0 + chunk_tokens, n_total)
+        lo = np.clip(c0 - starts[:-1], 0, new_len)
+        hi = np.clip(c1 - starts[:-1], 0, new_len)
+        cnt = hi - lo
+        qo_indptr = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+        kv_len = (prefix_len + hi).astype(np.int32)
+        app_dev = torch.as_tensor(qo_indptr).to(attn.device, non_blocking=False)
+        kvl_dev = torch.as_tensor(kv_len).to(attn.device, non_blocking=False)
+        kn, vn = k_new[c0:c1], v_new[c0:c1]
+        append_paged_kv(p, len(new_len), c1 - c0, app_dev, kvl_dev, page_indptr_dev, page_indices, kn, vn,
+                        kn.stride(0), kn.stride(1), k_pool, v_pool, ks, vs, stream)
+        attn.plan(qo_indptr, kv_len, page_indptr_host, stream=stream)
+        t = tensors_for(p, q[c0:c1], k_pool, v_pool, out[c0:c1], lse[c0:c1], page_indices=page_indices,
+                        layout=layout)
+        attn.run(t, stream=stream)

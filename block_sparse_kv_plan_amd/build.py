@@ -1,6 +1,8 @@
 """Build libbsk.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_kv_plan_amd.build      (or call build())
+    python block_sparse_kv_plan_amd/build.py      (or __graft_entry__.build())
+
+(run as a script, not ``-m``: importing the package would load the library being rebuilt)
 
 Every translation unit is compiled in parallel into ``_build/`` and linked
 into ``block_sparse_kv_plan_amd/libbsk.so``.  The planner (plan.cpp) is
@@ -25,7 +27,7 @@ ARCH = "gfx950"
 # packed-fp32 instructions are kept out of the device code on purpose
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops"]
-DEVICE_SOURCES = ["decode.hip", "prefill.hip", "merge.hip"]
+DEVICE_SOURCES = ["decode.hip", "prefill.hip", "merge.hip", "append.hip"]
 # per-file extras: the prefill kernel's logits are never NaN when they reach fmaxf (masked ones are
 # -inf), so it is built without NaN semantics and its max needs no operand canonicalisation
 EXTRA = {"prefill.hip": ["-fno-honor-nans"]}

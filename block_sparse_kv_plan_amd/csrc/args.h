@@ -41,6 +41,25 @@ struct AttnArgs {
   float scale_log2;     // sm_scale * log2(e): logits are kept in base 2
 };
 
+// Launch arguments of the append kernel (new tokens' K/V into the paged cache).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  int64_t new_st, new_sh;  // token / head strides (elements) of k_new and v_new
+  void* k_cache;
+  void* v_cache;
+  int64_t k_sp, k_sh, k_st;
+  int64_t v_sp, v_sh, v_st;
+  const int32_t* append_indptr;  // [batch + 1] new-token offsets (device)
+  const int32_t* kv_len;         // [batch] lengths after the append (device)
+  const int32_t* page_indptr;    // [batch + 1] page-list offsets (device)
+  const int32_t* page_indices;   // page lists (device)
+  int32_t batch;
+  int32_t n_total;
+  int32_t num_kv_heads;
+  int32_t page_shift;
+};
+
 struct MergeArgs {
   const int32_t* ws;
   const float* part_o;

@@ -374,6 +374,54 @@ bsk_status bsk_rope_table(float* table_dev, int32_t n_pos, int32_t head_dim, dou
   return BSK_OK;
 }
 
+bsk_status bsk_append_paged_kv(const bsk_problem* problem, int32_t batch, int32_t n_total,
+                               const int32_t* append_indptr, const int32_t* kv_len, const int32_t* kv_page_indptr,
+                               const int32_t* kv_page_indices, const void* k_new, const void* v_new,
+                               int64_t new_stride_tok, int64_t new_stride_head, void* k_cache, void* v_cache,
+                               int64_t k_stride_page, int64_t k_stride_head, int64_t k_stride_tok,
+                               int64_t v_stride_page, int64_t v_stride_head, int64_t v_stride_tok, void* stream) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (problem->kv_mode != BSK_KV_PAGED) return fail(BSK_ERR_INVALID_ARG, "append needs the paged layout");
+  if (batch < 0 || n_total < 0) return fail(BSK_ERR_INVALID_ARG, "negative batch / token count");
+  if (n_total == 0 || batch == 0) return BSK_OK;
+  if (!append_indptr || !kv_len || !kv_page_indptr || !kv_page_indices || !k_new || !v_new || !k_cache || !v_cache)
+    return fail(BSK_ERR_INVALID_ARG, "null argument");
+  const int64_t vec = 16 / (problem->dtype == BSK_DTYPE_BF16 ? 2 : 4);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(BSK_ERR_INVALID_ARG, "k_new, v_new and the pools must be 16-byte aligned");
+  if (new_stride_tok % vec || new_stride_head % vec || k_stride_page % vec || k_stride_head % vec ||
+      k_stride_tok % vec || v_stride_page % vec || v_stride_head % vec || v_stride_tok % vec)
+    return fail(BSK_ERR_INVALID_ARG, "strides must be multiples of 16 bytes");
+  if (new_stride_tok < 0 || new_stride_head < 0 || k_stride_page < 0 || k_stride_head < 0 || k_stride_tok < 0 ||
+      v_stride_page < 0 || v_stride_head < 0 || v_stride_tok < 0)
+    return fail(BSK_ERR_INVALID_ARG, "negative strides");
+  bsk::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_st = new_stride_tok;
+  a.new_sh = new_stride_head;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_sp = k_stride_page;
+  a.k_sh = k_stride_head;
+  a.k_st = k_stride_tok;
+  a.v_sp = v_stride_page;
+  a.v_sh = v_stride_head;
+  a.v_st = v_stride_tok;
+  a.append_indptr = append_indptr;
+  a.kv_len = kv_len;
+  a.page_indptr = kv_page_indptr;
+  a.page_indices = kv_page_indices;
+  a.batch = batch;
+  a.n_total = n_total;
+  a.num_kv_heads = problem->num_kv_heads;
+  a.page_shift = ilog2(problem->page_size);
+  hipError_t e = bsk::launch_append(problem->dtype, problem->head_dim, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return BSK_OK;
+}
+
 bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                             const void* int_ws_dev, const int64_t* row_offsets, void* k_out, void* v_out,
                             void* stream) {

@@ -16,6 +16,8 @@ hipError_t launch_prefill(int head_dim, bool dense, int tile_q, const AttnArgs& 
 const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q);
 int prefill_threads();
 
+hipError_t launch_append(int dtype, int head_dim, const AppendArgs& a, hipStream_t stream);
+
 hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t stream);
 hipError_t launch_merge_pair(const float* oa, const float* la, const float* ob, const float* lb, void* out,
                              float* lse_out, int rows, int D, int out_bf16, hipStream_t stream);

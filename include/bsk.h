@@ -275,6 +275,36 @@ bsk_status bsk_merge_state_pair(const float* o_a, const float* lse_a, const floa
 bsk_status bsk_rope_table(float* table_dev, int32_t n_pos, int32_t head_dim, double theta, void* stream);
 
 /*
+ * Append new tokens' K and V to a paged cache, the step before attention
+ * in chunked prefill ([FI-0.6, kernel types: Prefill]).  The n_r =
+ * append_indptr[r+1] - append_indptr[r] new tokens of request r become the
+ * last n_r tokens of its sequence: new token i (rows append_indptr[r] + i
+ * of k_new / v_new) is written at logical position kv_len[r] - n_r + i,
+ * i.e. page kv_page_indices[kv_page_indptr[r] + pos / page_size], slot
+ * pos % page_size ([FI-paper, methodology 1]).  kv_len is the length
+ * after the append.
+ *   problem: num_kv_heads, head_dim, dtype, page_size (PAGED) are used.
+ *   append_indptr [batch+1] (append_indptr[0] = 0, append_indptr[batch] =
+ *   n_total), kv_len [batch], kv_page_indptr [batch+1], kv_page_indices:
+ *   device int32.
+ *   k_new / v_new: device [n_total, num_kv_heads, head_dim] in dtype with
+ *   token / head strides new_stride_tok / new_stride_head (elements, the
+ *   last dimension contiguous, 16-byte aligned rows).
+ *   k_cache / v_cache: the pools, written in place, addressed as in
+ *   bsk_tensors with the given page / head / token strides (elements).
+ * Tokens whose position falls outside their request's page list (or below
+ * 0) are skipped.  The library reads and writes only the named buffers.
+ * Errors: INVALID_ARG (null pointers, negative sizes, misaligned
+ * pointers or strides, DENSE kv_mode), UNSUPPORTED (head_dim, dtype), HIP.
+ */
+bsk_status bsk_append_paged_kv(const bsk_problem* problem, int32_t batch, int32_t n_total,
+                               const int32_t* append_indptr, const int32_t* kv_len, const int32_t* kv_page_indptr,
+                               const int32_t* kv_page_indices, const void* k_new, const void* v_new,
+                               int64_t new_stride_tok, int64_t new_stride_head, void* k_cache, void* v_cache,
+                               int64_t k_stride_page, int64_t k_stride_head, int64_t k_stride_tok,
+                               int64_t v_stride_page, int64_t v_stride_head, int64_t v_stride_tok, void* stream);
+
+/*
  * Test hook for the block-sparse gather ([FI-0.6, architecture 1]): for
  * every plan item, copy the item's keys [kv_lo, kv_hi) of kv head h,
  * fetched through the same LDS-staged page-id path as the attention
