@@ -209,7 +209,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling aid: run just this workload (decode|prefill|append|composable|rope)")
+                    help="profiling aid: run just this workload (decode|prefill|append|strides|composable|rope)")
     ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
                     help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
     ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
@@ -366,6 +366,24 @@ def main():
             "tflops_incl_host_steps": round(flops / wall / 1e12, 1)}
         del attn, du
         torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "strides"):
+        log("strides: equal-stride (shared address) kernels vs independent K/V stride kernels, same data")
+        ab = {}
+        for name, b, tq, copies in (("decode", W.llama3_decode(), bsk.TILE_DECODE, 4),
+                                    ("prefill", W.ragged_prefill(), args.prefill_tile, 1)):
+            us = []
+            for ind in (0, 1):
+                runner = Runner(b, tq, copies=copies, device=device, independent_kv_strides=ind)
+                m = timed(runner, max(10, args.steps // 2) if name == "decode" else 8, 3)
+                us.append(m["kernel_s_mean"] * 1e6)
+                del runner
+                torch.cuda.empty_cache()
+            ab[name] = {"equal_strides_us": round(us[0], 2), "independent_strides_us": round(us[1], 2),
+                        "speedup": round(us[1] / us[0], 4)}
+        secondary["kv_stride_specialization"] = dict(
+            ab, note="K and V share page/head/token strides; independent_kv_strides=1 forces the general kernels "
+                     "on the same data (the pages report a 1.0456x geomean on B200)")
 
     if not args.no_secondary and args.only in ("", "rope"):
         log("rope: long-context streaming decode with fused RoPE, window 4096 + 4 sinks")

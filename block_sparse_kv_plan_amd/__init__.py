@@ -41,7 +41,8 @@ class Problem(ctypes.Structure):
                 ("sink", i32), ("rope_mode", i32), ("fused_merge", i32), ("rope_theta", f64), ("sm_scale", f32),
                 ("tile_q", i32), ("tile_kv", i32), ("num_workers", i32), ("split_factor", i32),
                 ("min_chunk", i32), ("max_chunk", i32), ("item_overhead", i32), ("max_batch", i32),
-                ("max_items_per_worker", i32), ("max_slots", i32), ("max_merge", i32)]
+                ("max_items_per_worker", i32), ("max_slots", i32), ("max_merge", i32),
+                ("independent_kv_strides", i32)]
 
 
 class PlanInfo(ctypes.Structure):

@@ -33,6 +33,12 @@ int ilog2(int x) {
   return s;
 }
 
+// The equal-stride kernels are used when the caller allows it and K and V share all strides.
+bool same_kv(const bsk_problem& p, const bsk_tensors& t) {
+  return p.independent_kv_strides == 0 && t.k_stride_head == t.v_stride_head && t.k_stride_tok == t.v_stride_tok &&
+         (p.kv_mode == BSK_KV_DENSE || t.k_stride_page == t.v_stride_page);
+}
+
 bool is_prefill_tile(int tile_q) { return tile_q == BSK_TILE_PREFILL || tile_q == BSK_TILE_PREFILL_256; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -56,6 +62,8 @@ bsk_status check_problem(const bsk_problem* p) {
     return fail(BSK_ERR_INVALID_ARG, "page_size must be a power of two <= 65536");
   if (p->causal != 0 && p->causal != 1) return fail(BSK_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (p->fused_merge != 0 && p->fused_merge != 1) return fail(BSK_ERR_INVALID_ARG, "fused_merge must be 0 or 1");
+  if (p->independent_kv_strides != 0 && p->independent_kv_strides != 1)
+    return fail(BSK_ERR_INVALID_ARG, "independent_kv_strides must be 0 or 1");
   if (p->window > 0 && p->sink < 0) return fail(BSK_ERR_INVALID_ARG, "sink must be >= 0");
   if (p->rope_mode < BSK_ROPE_NONE || p->rope_mode > BSK_ROPE_ABSOLUTE) return fail(BSK_ERR_INVALID_ARG, "rope_mode");
   if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
@@ -204,11 +212,12 @@ bsk_status bsk_device_workers(const bsk_problem* problem, int32_t* num_workers) 
   const void* fn = nullptr;
   int threads = 0;
   if (problem->tile_q == BSK_TILE_DECODE) {
-    fn = bsk::decode_kernel_ptr(problem->dtype, problem->head_dim, dense, problem->rope_mode);
+    fn = bsk::decode_kernel_ptr(problem->dtype, problem->head_dim, dense, problem->rope_mode,
+                                problem->independent_kv_strides == 0);
     threads = bsk::decode_threads();
   } else if (is_prefill_tile(problem->tile_q)) {
     if (problem->dtype == BSK_DTYPE_BF16 && problem->rope_mode == BSK_ROPE_NONE)
-      fn = bsk::prefill_kernel_ptr(problem->head_dim, dense, problem->tile_q);
+      fn = bsk::prefill_kernel_ptr(problem->head_dim, dense, problem->tile_q, problem->independent_kv_strides == 0);
     threads = bsk::prefill_threads();
   } else {
     return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16, 128 or 256");
@@ -291,7 +300,8 @@ bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info,
     return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for the paged layout only");
   const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
   hipError_t e = bsk::launch_decode(problem->dtype, problem->head_dim, problem->kv_mode == BSK_KV_DENSE,
-                                    problem->rope_mode, a, info->num_workers, static_cast<hipStream_t>(stream));
+                                    problem->rope_mode, same_kv(*problem, *t), a, info->num_workers,
+                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return BSK_OK;
 }
@@ -317,8 +327,8 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
       return fail(BSK_ERR_INVALID_ARG, "head / token strides too large for the prefill kernel's 32-bit row offsets");
   }
   const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
-  hipError_t e = bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, problem->tile_q, a,
-                                     info->num_workers, static_cast<hipStream_t>(stream));
+  hipError_t e = bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, problem->tile_q,
+                                     same_kv(*problem, *t), a, info->num_workers, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return BSK_OK;
 }

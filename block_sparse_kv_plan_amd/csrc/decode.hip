@@ -100,7 +100,8 @@ __device__ __forceinline__ i16x4 gather_e(const u32x4& a, const u32x4& b, const 
   return __builtin_bit_cast(i16x4, r);
 }
 
-template <typename T, int D, bool DENSE, int ROPE>
+// SAME: K and V share page/head/token strides, so one offset serves both tensors.
+template <typename T, int D, bool DENSE, int ROPE, bool SAME>
 __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode_kernel(AttnArgs a) {
   constexpr bool BF = __is_same(T, __bf16);
   constexpr int NKS = BF ? D / 32 : D / 4;  // MFMA k-steps over d for the logits
@@ -213,7 +214,10 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
     // element offsets of key t of kv head h (K and V strides may differ)
     auto key_offsets = [&](int t, int64_t& ko, int64_t& vo) {
       ko = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
-      vo = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
+      if constexpr (SAME)
+        vo = ko;
+      else
+        vo = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
     };
 
     // masked, scaled logits -> probabilities; online-softmax state update
@@ -441,46 +445,59 @@ __global__ __launch_bounds__(kDecThreads, ROPE == ROPE_NONE ? 3 : 2) void decode
 
 // ---------------------------------------------------------------- host launchers
 
-template <typename T, int D, bool DENSE, int ROPE>
+template <typename T, int D, bool DENSE, int ROPE, bool SAME>
 hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<T, D, DENSE, ROPE>), dim3(grid), dim3(kDecThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, DENSE, ROPE, SAME>), dim3(grid), dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool DENSE, int ROPE>
+template <typename T, int D, bool DENSE, int ROPE, bool SAME>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&decode_kernel<T, D, DENSE, ROPE>);
+  return reinterpret_cast<const void*>(&decode_kernel<T, D, DENSE, ROPE, SAME>);
 }
 
-#define BSK_DEC_VARIANTS(X)             \
-  X(__bf16, 128, false, ROPE_NONE)      \
-  X(__bf16, 128, true, ROPE_NONE)       \
-  X(__bf16, 64, false, ROPE_NONE)       \
-  X(__bf16, 64, true, ROPE_NONE)        \
-  X(__bf16, 128, false, ROPE_STREAMING) \
-  X(__bf16, 128, false, ROPE_ABSOLUTE)  \
-  X(__bf16, 64, false, ROPE_STREAMING)  \
-  X(__bf16, 64, false, ROPE_ABSOLUTE)   \
-  X(float, 64, false, ROPE_NONE)        \
-  X(float, 64, true, ROPE_NONE)         \
-  X(float, 128, false, ROPE_NONE)       \
-  X(float, 128, true, ROPE_NONE)
+// (element type, head_dim, dense KV, RoPE mode, equal K/V strides); f32 is built with
+// independent strides only
+#define BSK_DEC_VARIANTS(X)                    \
+  X(__bf16, 128, false, ROPE_NONE, true)       \
+  X(__bf16, 128, true, ROPE_NONE, true)        \
+  X(__bf16, 64, false, ROPE_NONE, true)        \
+  X(__bf16, 64, true, ROPE_NONE, true)         \
+  X(__bf16, 128, false, ROPE_STREAMING, true)  \
+  X(__bf16, 128, false, ROPE_ABSOLUTE, true)   \
+  X(__bf16, 64, false, ROPE_STREAMING, true)   \
+  X(__bf16, 64, false, ROPE_ABSOLUTE, true)    \
+  X(__bf16, 128, false, ROPE_NONE, false)      \
+  X(__bf16, 128, true, ROPE_NONE, false)       \
+  X(__bf16, 64, false, ROPE_NONE, false)       \
+  X(__bf16, 64, true, ROPE_NONE, false)        \
+  X(__bf16, 128, false, ROPE_STREAMING, false) \
+  X(__bf16, 128, false, ROPE_ABSOLUTE, false)  \
+  X(__bf16, 64, false, ROPE_STREAMING, false)  \
+  X(__bf16, 64, false, ROPE_ABSOLUTE, false)   \
+  X(float, 64, false, ROPE_NONE, false)        \
+  X(float, 64, true, ROPE_NONE, false)         \
+  X(float, 128, false, ROPE_NONE, false)       \
+  X(float, 128, true, ROPE_NONE, false)
 
-// dtype: 0 f32, 1 bf16.  Returns hipErrorInvalidValue for combinations not built.
-hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, const AttnArgs& a, int grid,
+// dtype: 0 f32, 1 bf16.  same: K and V strides are equal (ignored for f32).  Returns
+// hipErrorInvalidValue for combinations not built.
+hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, bool same, const AttnArgs& a, int grid,
                          hipStream_t stream) {
-#define BSK_DEC(T, D, DN, R)                                                              \
-  if ((dtype == 1) == __is_same(T, __bf16) && head_dim == D && dense == DN && rope == R) \
-    return launch_one<T, D, DN, R>(a, grid, stream);
+  if (dtype == 0) same = false;
+#define BSK_DEC(T, D, DN, R, S)                                                                        \
+  if ((dtype == 1) == __is_same(T, __bf16) && head_dim == D && dense == DN && rope == R && same == S) \
+    return launch_one<T, D, DN, R, S>(a, grid, stream);
   BSK_DEC_VARIANTS(BSK_DEC)
 #undef BSK_DEC
   return hipErrorInvalidValue;
 }
 
-const void* decode_kernel_ptr(int dtype, int head_dim, bool dense, int rope) {
-#define BSK_DEC(T, D, DN, R)                                                              \
-  if ((dtype == 1) == __is_same(T, __bf16) && head_dim == D && dense == DN && rope == R) \
-    return kernel_ptr<T, D, DN, R>();
+const void* decode_kernel_ptr(int dtype, int head_dim, bool dense, int rope, bool same) {
+  if (dtype == 0) same = false;
+#define BSK_DEC(T, D, DN, R, S)                                                                        \
+  if ((dtype == 1) == __is_same(T, __bf16) && head_dim == D && dense == DN && rope == R && same == S) \
+    return kernel_ptr<T, D, DN, R, S>();
   BSK_DEC_VARIANTS(BSK_DEC)
 #undef BSK_DEC
   return nullptr;

@@ -7,13 +7,14 @@
 
 namespace bsk {
 
-hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, const AttnArgs& a, int grid,
+hipError_t launch_decode(int dtype, int head_dim, bool dense, int rope, bool same, const AttnArgs& a, int grid,
                          hipStream_t stream);
-const void* decode_kernel_ptr(int dtype, int head_dim, bool dense, int rope);
+const void* decode_kernel_ptr(int dtype, int head_dim, bool dense, int rope, bool same);
 int decode_threads();
 
-hipError_t launch_prefill(int head_dim, bool dense, int tile_q, const AttnArgs& a, int grid, hipStream_t stream);
-const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q);
+hipError_t launch_prefill(int head_dim, bool dense, int tile_q, bool same, const AttnArgs& a, int grid,
+                          hipStream_t stream);
+const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q, bool same);
 int prefill_threads();
 
 hipError_t launch_append(int dtype, int head_dim, const AppendArgs& a, hipStream_t stream);

@@ -68,7 +68,9 @@ __device__ __forceinline__ bf16x8 ds_read_tr_pair(const unsigned short* p0, cons
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int D, bool DENSE, int NB>
+// SAME: K and V share page/head/token strides; a V address is the K address plus the K-to-V
+// pointer distance.
+template <int D, bool DENSE, int NB, bool SAME>
 __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(AttnArgs a) {
   constexpr int ROWS = kPreWaves * 16 * NB;  // query rows per item (the plan's tile_q)
   constexpr int WROWS = 16 * NB;             // rows per wave
@@ -185,7 +187,8 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
     for (int p = 0; p < NP; ++p) {
       const int tok = DENSE ? trow[p] : (trow[p] & pmask);
       koff[p] = uint32_t(2 * (int64_t(h) * a.k_sh + int64_t(tok) * a.k_st) + 16 * ck[p]);
-      voff[p] = uint32_t(2 * (int64_t(h) * a.v_sh + int64_t(tok) * a.v_st) + 16 * cv[p]);
+      voff[p] = SAME ? koff[p] - 16 * ck[p] + 16 * cv[p]
+                     : uint32_t(2 * (int64_t(h) * a.v_sh + int64_t(tok) * a.v_st) + 16 * cv[p]);
     }
     const int p0 = kv_lo >> a.page_shift;
 
@@ -209,8 +212,12 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
           for (int p = 0; p < NP; ++p) {
             const uint32_t page = uint32_t(s_pages[sb + (trow[p] >> a.page_shift)]);
             const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
-            dma16(kb + (uint64_t(page) * k_page_bytes + koff[p]), lk0 + lo);
-            dma16(vb + (uint64_t(page) * v_page_bytes + voff[p]), lv0 + lo);
+            const uint64_t pk = uint64_t(page) * k_page_bytes + koff[p];
+            dma16(kb + pk, lk0 + lo);
+            if constexpr (SAME)  // the V row sits at the same offset; only its 16-byte chunk differs
+              dma16(vb + (int64_t(pk) + 16 * (cv[p] - ck[p])), lv0 + lo);
+            else
+              dma16(vb + (uint64_t(page) * v_page_bytes + voff[p]), lv0 + lo);
           }
         }
       } else {
@@ -219,7 +226,8 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
         for (int p = 0; p < NP; ++p) {
           const int t = min(kt + trow[p], kv_hi - 1);
           const int64_t ko = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
-          const int64_t vo = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
+          const int64_t vo =
+              SAME ? ko : kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
           const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
           dma16(Kp + ko + 8 * ck[p], lk0 + lo);
           dma16(Vp + vo + 8 * cv[p], lv0 + lo);
@@ -398,35 +406,41 @@ __global__ __launch_bounds__(kPreThreads, NB <= 2 ? 2 : 1) void prefill_kernel(A
   }
 }
 
-hipError_t launch_prefill(int head_dim, bool dense, int tile_q, const AttnArgs& a, int grid, hipStream_t stream) {
-#define BSK_PRE(D, DN, NB)                                                                         \
-  if (head_dim == D && dense == DN && tile_q == 64 * NB) {                                         \
-    hipLaunchKernelGGL((prefill_kernel<D, DN, NB>), dim3(grid), dim3(kPreThreads), 0, stream, a); \
-    return hipGetLastError();                                                                      \
+#define BSK_PRE_VARIANTS(X) \
+  X(128, false, 2, true)        \
+  X(128, true, 2, true)         \
+  X(64, false, 2, true)         \
+  X(64, true, 2, true)          \
+  X(128, false, 4, true)        \
+  X(128, true, 4, true)         \
+  X(64, false, 4, true)         \
+  X(64, true, 4, true)          \
+  X(128, false, 2, false)       \
+  X(128, true, 2, false)        \
+  X(64, false, 2, false)        \
+  X(64, true, 2, false)         \
+  X(128, false, 4, false)       \
+  X(128, true, 4, false)        \
+  X(64, false, 4, false)        \
+  X(64, true, 4, false)
+
+hipError_t launch_prefill(int head_dim, bool dense, int tile_q, bool same, const AttnArgs& a, int grid,
+                          hipStream_t stream) {
+#define BSK_PRE(D, DN, NB, S)                                                                          \
+  if (head_dim == D && dense == DN && tile_q == 64 * NB && same == S) {                                \
+    hipLaunchKernelGGL((prefill_kernel<D, DN, NB, S>), dim3(grid), dim3(kPreThreads), 0, stream, a); \
+    return hipGetLastError();                                                                          \
   }
-  BSK_PRE(128, false, 2)
-  BSK_PRE(128, true, 2)
-  BSK_PRE(64, false, 2)
-  BSK_PRE(64, true, 2)
-  BSK_PRE(128, false, 4)
-  BSK_PRE(128, true, 4)
-  BSK_PRE(64, false, 4)
-  BSK_PRE(64, true, 4)
+  BSK_PRE_VARIANTS(BSK_PRE)
 #undef BSK_PRE
   return hipErrorInvalidValue;
 }
 
-const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q) {
-#define BSK_PRE_PTR(D, DN, NB) \
-  if (head_dim == D && dense == DN && tile_q == 64 * NB) return reinterpret_cast<const void*>(&prefill_kernel<D, DN, NB>);
-  BSK_PRE_PTR(128, false, 2)
-  BSK_PRE_PTR(128, true, 2)
-  BSK_PRE_PTR(64, false, 2)
-  BSK_PRE_PTR(64, true, 2)
-  BSK_PRE_PTR(128, false, 4)
-  BSK_PRE_PTR(128, true, 4)
-  BSK_PRE_PTR(64, false, 4)
-  BSK_PRE_PTR(64, true, 4)
+const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q, bool same) {
+#define BSK_PRE_PTR(D, DN, NB, S)                                      \
+  if (head_dim == D && dense == DN && tile_q == 64 * NB && same == S) \
+    return reinterpret_cast<const void*>(&prefill_kernel<D, DN, NB, S>);
+  BSK_PRE_VARIANTS(BSK_PRE_PTR)
 #undef BSK_PRE_PTR
   return nullptr;
 }

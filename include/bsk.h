@@ -108,6 +108,11 @@ typedef struct bsk_problem {
   int32_t max_items_per_worker;
   int32_t max_slots;     /* partial-state slots in the float workspace         */
   int32_t max_merge;     /* merge-table entries                                */
+  /* K/V stride specialisation ([FI-PR5329]): 0 (default) -- when K and V
+     have equal page/head/token strides the bf16 kernels form one address
+     per key and reach V through the K-to-V pointer distance; 1 -- always
+     use the kernels that address K and V with their own strides */
+  int32_t independent_kv_strides;
 } bsk_problem;
 
 /* Filled by bsk_plan; passed unchanged to run/merge. */

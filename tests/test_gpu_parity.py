@@ -337,3 +337,36 @@ def test_graph_capture_replan_replay():
         bt.kv_len = kv.astype(np.int32)
         compare(bt, out.double().cpu().numpy(), lse.double().cpu().numpy())
         _ = (out * 2).sum().item()  # eager work between replays
+
+
+# ------------------------------------------------------------------ K/V stride specialisation
+
+@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL, bsk.TILE_PREFILL_256])
+def test_kv_stride_specialisation_is_bit_identical(tile_q):
+    """With equal K/V strides the shared-address kernels and the independent-stride kernels
+    compute exactly the same result (only the addressing differs)."""
+    kv = np.array([300, 129, 77, 1000])
+    qo = np.array([1, 1, 1, 1]) if tile_q == bsk.TILE_DECODE else np.array([300, 40, 77, 130])
+    b = small(97, kv, qo=qo, Hq=16, Hk=4, d=128, causal=True)
+    say(f"kv stride specialisation tile_q={tile_q}")
+    O1, L1, _, _ = run(b, tile_q=tile_q, num_workers=24, min_chunk=64, independent_kv_strides=0)
+    O2, L2, _, _ = run(b, tile_q=tile_q, num_workers=24, min_chunk=64, independent_kv_strides=1)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    compare(b, O1, L1)
+
+
+@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL])
+def test_independent_v_strides(tile_q):
+    """V in a pool with padded rows (its own strides) goes through the independent-stride kernels."""
+    kv = np.array([300, 129, 77, 1000])
+    qo = np.array([1, 1, 1, 1]) if tile_q == bsk.TILE_DECODE else np.array([300, 40, 77, 130])
+    b = small(98, kv, qo=qo, Hq=16, Hk=4, d=128, causal=True)
+    d = upload(b)
+    v = d["v"]
+    vpad = torch.full(v.shape[:-1] + (v.shape[-1] + 16,), float("nan"), dtype=v.dtype, device=v.device)
+    vpad[..., :v.shape[-1]] = v
+    d["v"] = vpad[..., :v.shape[-1]]
+    assert d["v"].stride() != d["k"].stride()
+    say(f"independent V strides tile_q={tile_q}")
+    O, L, _, _ = run(b, tile_q=tile_q, num_workers=24, min_chunk=64, dev_tensors=d)
+    compare(b, O, L)
