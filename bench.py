@@ -78,13 +78,15 @@ def make_attention(batch, tile_q, out_dtype, device, **kw):
     import block_sparse_kv_plan_amd as bsk
     from block_sparse_kv_plan_amd.attention import BatchAttention
     rope_mode = {"none": bsk.ROPE_NONE, "streaming": bsk.ROPE_STREAMING, "absolute": bsk.ROPE_ABSOLUTE}[batch.rope]
-    return BatchAttention.create(
+    args = dict(
         device=device, num_qo_heads=batch.num_qo_heads, num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim,
         dtype=bsk.DTYPE_BF16 if batch.dtype == "bf16" else bsk.DTYPE_F32, out_dtype=out_dtype,
         kv_mode=bsk.KV_DENSE if batch.kv_mode == "dense" else bsk.KV_PAGED,
         page_size=batch.page_size if batch.kv_mode == "paged" else 16, causal=batch.causal, window=batch.window,
         sink=batch.sink, rope_mode=rope_mode, rope_theta=batch.rope_theta, sm_scale=batch.sm_scale,
-        tile_q=tile_q, max_batch=max(1, batch.batch_size), **kw)
+        tile_q=tile_q, max_batch=max(1, batch.batch_size))
+    args.update(kw)
+    return BatchAttention.create(**args)
 
 
 class Runner:
@@ -398,7 +400,43 @@ def main():
             "frac_of_hbm_peak": round(nbytes / m["kernel_s_mean"] / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2), "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
             "step_us": round(m["wall_s"] * 1e6, 1), "algorithmic_bytes": nbytes}
-        del runner
+        # unfused reference point: rotate the visible keys and the query into scratch, then a plain
+        # windowed decode over (rotated K, V); same bytes credited as the fused kernel's
+        from block_sparse_kv_plan_amd.attention import tensors_for
+        d0 = runner.dev[0]
+        k_out = torch.empty_like(d0["k"])
+        q_out = torch.empty_like(d0["q"])
+        i32 = lambda x: torch.as_tensor(np.asarray(x, dtype=np.int32), device=device)
+        qo_d, kvl_d, pip_d = i32(b.qo_indptr), i32(b.kv_len), i32(runner.kv_indptr)
+        rprob = runner.attn[0].problem
+        t_rot = tensors_for(rprob, d0["q"], d0["k"], d0["v"], runner.out, runner.lse, page_indices=d0["pages"],
+                            rope=runner.rope)
+        plain = make_attention(b, bsk.TILE_DECODE, 0, device, rope_mode=bsk.ROPE_NONE)
+        t_plain = tensors_for(plain.problem, q_out, k_out, d0["v"], runner.out, runner.lse, page_indices=d0["pages"])
+        stream = torch.cuda.current_stream()
+        plain.plan(b.qo_indptr, b.kv_len, runner.kv_indptr, stream=stream)
+        reps = max(10, args.steps // 2)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 3)]
+        for i in range(reps + 3):
+            evs[i][0].record(stream)
+            bsk.rope_apply(rprob, b.batch_size, int(b.kv_len.max()), qo_d, kvl_d, pip_d, t_rot, q_out,
+                           q_out.stride(0), q_out.stride(1), k_out, stream)
+            evs[i][1].record(stream)
+            plain.run(t_plain, stream=stream, merge=False)
+            evs[i][2].record(stream)
+        torch.cuda.synchronize()
+        rot_us = sum(e[0].elapsed_time(e[1]) for e in evs[3:]) / reps * 1e3
+        dec_us = sum(e[1].elapsed_time(e[2]) for e in evs[3:]) / reps * 1e3
+        fused_us = m["kernel_s_mean"] * 1e6
+        secondary["unfused_rope_baseline"] = {
+            "workload": "the streaming-RoPE decode above, RoPE applied by a separate pass (visible keys and the "
+                        "query rotated into scratch, bf16), then the plain windowed decode",
+            "rotate_us": round(rot_us, 2), "decode_us": round(dec_us, 2), "unfused_us": round(rot_us + dec_us, 2),
+            "fused_us": round(fused_us, 2), "fused_speedup": round((rot_us + dec_us) / fused_us, 3),
+            "fused_gbs": round(nbytes / fused_us / 1e3, 1), "unfused_gbs": round(nbytes / (rot_us + dec_us) / 1e3, 1),
+            "note": "effective bandwidth = the fused kernel's algorithmic bytes / time (the pages report 1.6-3.7x "
+                    "for fused RoPE + attention)"}
+        del runner, plain, k_out, q_out
         torch.cuda.empty_cache()
 
     if not args.no_secondary and args.only in ("", "composable"):

@@ -75,6 +75,7 @@ _sig = {
     "bsk_merge_state_pair": [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp],
     "bsk_rope_table": [vp, i32, i32, f64, vp],
     "bsk_debug_gather": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp, vp, vp],
+    "bsk_rope_apply": [P(Problem), i32, i32, vp, vp, vp, P(Tensors), vp, i64, i64, vp, vp],
     "bsk_append_paged_kv": [P(Problem), i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64,
                             i64, vp],
 }
@@ -188,6 +189,13 @@ def append_paged_kv(problem: Problem, batch: int, n_total: int, append_indptr, k
                                  _ptr(kv_page_indptr), _ptr(kv_page_indices), _ptr(k_new), _ptr(v_new),
                                  int(new_stride_tok), int(new_stride_head), _ptr(k_cache), _ptr(v_cache),
                                  *(int(x) for x in k_strides), *(int(x) for x in v_strides), _stream(stream)))
+
+
+def rope_apply(problem: Problem, batch: int, max_kv_len: int, qo_indptr, kv_len, kv_page_indptr, tensors: Tensors,
+               q_out, qo_stride_tok: int, qo_stride_head: int, k_out, stream=None):
+    _ok(_lib.bsk_rope_apply(ctypes.byref(problem), batch, max_kv_len, _ptr(qo_indptr), _ptr(kv_len),
+                            _ptr(kv_page_indptr), ctypes.byref(tensors), _ptr(q_out), int(qo_stride_tok),
+                            int(qo_stride_head), _ptr(k_out), _stream(stream)))
 
 
 def debug_gather(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, row_offsets, k_out, v_out,

@@ -60,6 +60,28 @@ struct AppendArgs {
   int32_t page_shift;
 };
 
+// Launch arguments of the unfused RoPE pass (rotated visible keys and query into scratch).
+struct RopeApplyArgs {
+  const void* q;
+  int64_t q_st, q_sh;
+  void* q_out;
+  int64_t qo_st, qo_sh;
+  const void* k;
+  void* k_out;  // same strides as k
+  int64_t k_sp, k_sh, k_st;
+  const int32_t* qo_indptr;     // [batch + 1] (device)
+  const int32_t* kv_len;        // [batch] (device)
+  const int32_t* page_indptr;   // [batch + 1] (device)
+  const int32_t* page_indices;  // (device)
+  const float* rope;            // [n_pos][D/2][2]
+  int32_t rope_n_pos;
+  int32_t batch;
+  int32_t num_qo_heads, num_kv_heads;
+  int32_t page_shift;
+  int32_t window, sink;
+  int32_t streaming;  // 1: rank in the visible set, 0: token index
+};
+
 struct MergeArgs {
   const int32_t* ws;
   const float* part_o;

@@ -432,6 +432,59 @@ bsk_status bsk_append_paged_kv(const bsk_problem* problem, int32_t batch, int32_
   return BSK_OK;
 }
 
+bsk_status bsk_rope_apply(const bsk_problem* problem, int32_t batch, int32_t max_kv_len, const int32_t* qo_indptr,
+                          const int32_t* kv_len, const int32_t* kv_page_indptr, const bsk_tensors* t, void* q_out,
+                          int64_t qo_stride_tok, int64_t qo_stride_head, void* k_out, void* stream) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (problem->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the unfused RoPE pass is bf16 only");
+  if (problem->kv_mode != BSK_KV_PAGED) return fail(BSK_ERR_UNSUPPORTED, "the unfused RoPE pass needs paged KV");
+  if (problem->rope_mode == BSK_ROPE_NONE) return fail(BSK_ERR_INVALID_ARG, "rope_mode is NONE");
+  if (batch < 0 || max_kv_len < 0) return fail(BSK_ERR_INVALID_ARG, "negative batch / max_kv_len");
+  if (batch == 0) return BSK_OK;
+  if (!t || !qo_indptr || !kv_len || !kv_page_indptr || !t->q || !t->k || !t->kv_page_indices || !t->rope_cos_sin ||
+      !q_out || !k_out)
+    return fail(BSK_ERR_INVALID_ARG, "null argument");
+  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
+      !aligned(t->rope_cos_sin, 16))
+    return fail(BSK_ERR_INVALID_ARG, "q, k, q_out, k_out and the table must be 16-byte aligned");
+  if (t->q_stride_tok % 8 || t->q_stride_head % 8 || qo_stride_tok % 8 || qo_stride_head % 8 ||
+      t->k_stride_page % 8 || t->k_stride_head % 8 || t->k_stride_tok % 8)
+    return fail(BSK_ERR_INVALID_ARG, "strides must be multiples of 16 bytes");
+  const int64_t max_visible = problem->window > 0 ? std::min<int64_t>(max_kv_len, int64_t(problem->window) + problem->sink)
+                                                  : max_kv_len;
+  const int64_t need = problem->rope_mode == BSK_ROPE_STREAMING ? max_visible : max_kv_len;
+  if (t->rope_n_pos < need) return fail(BSK_ERR_INVALID_ARG, "rope table has too few positions");
+  bsk::RopeApplyArgs a;
+  a.q = t->q;
+  a.q_st = t->q_stride_tok;
+  a.q_sh = t->q_stride_head;
+  a.q_out = q_out;
+  a.qo_st = qo_stride_tok;
+  a.qo_sh = qo_stride_head;
+  a.k = t->k;
+  a.k_out = k_out;
+  a.k_sp = t->k_stride_page;
+  a.k_sh = t->k_stride_head;
+  a.k_st = t->k_stride_tok;
+  a.qo_indptr = qo_indptr;
+  a.kv_len = kv_len;
+  a.page_indptr = kv_page_indptr;
+  a.page_indices = t->kv_page_indices;
+  a.rope = t->rope_cos_sin;
+  a.rope_n_pos = t->rope_n_pos;
+  a.batch = batch;
+  a.num_qo_heads = problem->num_qo_heads;
+  a.num_kv_heads = problem->num_kv_heads;
+  a.page_shift = ilog2(problem->page_size);
+  a.window = problem->window > 0 ? problem->window : 0;
+  a.sink = problem->window > 0 ? problem->sink : 0;
+  a.streaming = problem->rope_mode == BSK_ROPE_STREAMING;
+  hipError_t e = bsk::launch_rope_apply(problem->head_dim, a, int(max_visible), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope apply launch");
+  return BSK_OK;
+}
+
 bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                             const void* int_ws_dev, const int64_t* row_offsets, void* k_out, void* v_out,
                             void* stream) {

@@ -310,6 +310,31 @@ bsk_status bsk_append_paged_kv(const bsk_problem* problem, int32_t batch, int32_
                                int64_t v_stride_page, int64_t v_stride_head, int64_t v_stride_tok, void* stream);
 
 /*
+ * Unfused RoPE, the reference point of the fused-RoPE decode ([FI-paper,
+ * results: fused RoPE + attention kernel]): for every request (one query
+ * per request: its last token at kv_len - 1), rotate the keys that query
+ * sees -- with problem.window > 0 the window [kv_len - window, kv_len)
+ * plus the first problem.sink tokens, else all kv_len keys -- from the
+ * paged pool t->k into k_out at the same page slots (same strides as
+ * t->k), and rotate the query row (token qo_indptr[r+1] - 1, all q heads)
+ * from t->q into q_out.  Positions per problem.rope_mode: STREAMING = rank
+ * in the visible set (the query last), ABSOLUTE = token index.  Rotate-half
+ * with the table t->rope_cos_sin (bsk_rope_table), fp32 arithmetic, bf16
+ * results.  A plain decode (rope_mode NONE, same window/sink) over
+ * (q_out, k_out, t->v) then computes the RoPE attention.
+ *   qo_indptr [batch+1], kv_len [batch], kv_page_indptr [batch+1]: device
+ *   int32; max_kv_len: host bound on kv_len (sizes the grid).
+ *   q_out: [tokens, Hq, head_dim] bf16 with strides qo_stride_tok/head.
+ * Slots of k_out outside the visible keys are not written.
+ * Errors: INVALID_ARG (null pointers, rope_mode NONE, misaligned strides,
+ * table shorter than the positions), UNSUPPORTED (dtype not bf16, DENSE,
+ * head_dim), HIP.
+ */
+bsk_status bsk_rope_apply(const bsk_problem* problem, int32_t batch, int32_t max_kv_len, const int32_t* qo_indptr,
+                          const int32_t* kv_len, const int32_t* kv_page_indptr, const bsk_tensors* t, void* q_out,
+                          int64_t qo_stride_tok, int64_t qo_stride_head, void* k_out, void* stream);
+
+/*
  * Test hook for the block-sparse gather ([FI-0.6, architecture 1]): for
  * every plan item, copy the item's keys [kv_lo, kv_hi) of kv head h,
  * fetched through the same LDS-staged page-id path as the attention
