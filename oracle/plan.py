@@ -19,6 +19,10 @@ independent implementation can match it bit for bit:
    keys [lo, hi) with hi = min(kv_len, qpos(i_hi)+1) if causal else kv_len,
    lo = max(0, qpos(i_lo) - window + 1) if window > 0 else 0, plus the sink
    range [0, min(sink, lo)) when window > 0 and lo > 0.
+   Two tile classes (one launch for a mixed batch): with decode_tile_q > 0,
+   a request whose rows fit one decode tile (qo_len * g <= decode_tile_q)
+   gets a single unit per kv head of class 1 (the decode tile); every other
+   request is tiled by tile_q as above (class 0).  Nothing else changes.
 2. Total cost C = sum over units of (hi - lo) + |sink range|.
 3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W*split_factor)), tile_kv)),
    then min(L_c, max_chunk) when max_chunk > 0.
@@ -74,6 +78,7 @@ class PlanParams:
     causal: bool = False
     window: int = 0
     sink: int = 0
+    decode_tile_q: int = 0  # > 0: requests with qo_len * g <= decode_tile_q use one decode-class tile
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -92,14 +97,18 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
     W = p.num_workers
 
     units = []  # (r, h, row_lo, row_hi, lo, hi, sink_hi)
+    unit_class = []
     for r, (Q, L) in enumerate(zip(qo_len, kv_len)):
         if Q == 0 or L == 0:
             continue
         rows = Q * g
+        small = p.decode_tile_q > 0 and rows <= p.decode_tile_q
+        tq = p.decode_tile_q if small else p.tile_q
         for h in range(p.num_kv_heads):
-            for t in range(_ceil_div(rows, p.tile_q)):
-                row_lo = t * p.tile_q
-                row_hi = min(rows, (t + 1) * p.tile_q)
+            for t in range(_ceil_div(rows, tq)):
+                row_lo = t * tq
+                row_hi = min(rows, (t + 1) * tq)
+                unit_class.append(1 if small else 0)
                 i_lo, i_hi = row_lo // g, (row_hi - 1) // g
                 qpos_lo, qpos_hi = L - Q + i_lo, L - Q + i_hi
                 hi = min(L, qpos_hi + 1) if p.causal else L
@@ -113,9 +122,10 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
         Lc = min(Lc, p.max_chunk)
 
     items = []   # (r, h, row_lo, row_hi, kv_lo, kv_hi, slot)
+    item_class = []
     merges = []  # (r, h, row_lo, row_hi, first_slot, n)
     next_slot = 0
-    for (r, h, row_lo, row_hi, lo, hi, sink_hi) in units:
+    for u, (r, h, row_lo, row_hi, lo, hi, sink_hi) in enumerate(units):
         chunks = [(max(lo, k * Lc), min(hi, (k + 1) * Lc)) for k in range(lo // Lc, (hi - 1) // Lc + 1)]
         if sink_hi > 0:
             chunks.append((0, sink_hi))
@@ -125,9 +135,11 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
             merges.append((r, h, row_lo, row_hi, first, len(chunks)))
             for c, (a, b) in enumerate(chunks):
                 items.append((r, h, row_lo, row_hi, a, b, first + c))
+                item_class.append(unit_class[u])
         else:
             a, b = chunks[0]
             items.append((r, h, row_lo, row_hi, a, b, -1))
+            item_class.append(unit_class[u])
 
     cost = [(it[5] - it[4]) + p.item_overhead for it in items]
     order = sorted(range(len(items)), key=lambda i: (-cost[i], i))
@@ -154,6 +166,7 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
         "total_cost": C,
         "chunk": Lc,
         "items": np.asarray(items, dtype=np.int64).reshape(-1, 7),
+        "item_class": np.asarray(item_class, dtype=np.int64),
         "cost": np.asarray(cost, dtype=np.int64),
         "worker_items": worker_items,
         "load": np.asarray(load, dtype=np.int64),

@@ -498,3 +498,59 @@ def test_append_in_two_steps_equals_one():
     k2, v2 = oracle.append_paged_kv(k1, v1, c["indptr"], c["perm"], c["ps"], app2, c["after"],
                                     c["kn"][idx2.astype(int)], c["vn"][idx2.astype(int)])
     assert np.array_equal(k2, one[0]) and np.array_equal(v2, one[1])
+
+
+# ------------------------------------------------------------------ two tile classes (mixed launches)
+
+def _rows_cover_exactly_once(qo, kv, plan, g, nh):
+    """Every (request, kv head, query row) belongs to exactly one unit."""
+    seen = {}
+    for (r, h, row_lo, row_hi, *_rest) in plan["units"]:
+        for row in range(row_lo, row_hi):
+            seen[(int(r), int(h), row)] = seen.get((int(r), int(h), row), 0) + 1
+    want = {(r, h, row): 1 for r in range(len(qo)) if qo[r] > 0 and kv[r] > 0
+            for h in range(nh) for row in range(int(qo[r]) * g)}
+    assert seen == want
+
+
+@pytest.mark.parametrize("causal,window,sink", [(True, 0, 0), (True, 40, 4)])
+def test_mixed_plan_tiles_and_coverage(causal, window, sink):
+    """Requests whose rows fit a decode tile get one decode-class unit per head; the others are
+    tiled by tile_q; rows and visible keys are covered exactly once and the item classes follow
+    their requests."""
+    rng = np.random.default_rng(12)
+    kv = rng.integers(1, 400, size=10)
+    qo = np.minimum(kv, np.array([1, 3, 4, 5, 40, 1, 2, 100, 4, 9]))
+    p = _params(tile_q=128, tile_kv=64, min_chunk=64, decode_tile_q=16, causal=causal, window=window, sink=sink)
+    g = p.num_qo_heads // p.num_kv_heads   # 4: qo_len <= 4 fits a 16-row tile
+    plan = oracle.plan_ref(qo, kv, p)
+    _coverage_check(qo, kv, p, plan)
+    _rows_cover_exactly_once(qo, kv, plan, g, p.num_kv_heads)
+    for it, cls in zip(plan["items"], plan["item_class"]):
+        r = int(it[0])
+        small = int(qo[r]) * g <= 16
+        assert cls == (1 if small else 0)
+        assert it[3] - it[2] <= (16 if small else 128)
+    # per request and head: one unit exactly when the request is decode-class
+    for r in range(len(qo)):
+        n_units = sum(1 for u in plan["units"] if u[0] == r and u[1] == 0)
+        if qo[r] * g <= 16:
+            assert n_units == 1
+        else:
+            assert n_units == -(-int(qo[r]) * g // 128)
+
+
+def test_mixed_plan_without_decode_class_is_unchanged():
+    rng = np.random.default_rng(13)
+    kv = rng.integers(50, 400, size=6)
+    qo = np.minimum(kv, rng.integers(5, 60, size=6))  # qo_len * g > 16 everywhere
+    base = _params(tile_q=128, tile_kv=64, min_chunk=64, causal=True)
+    a = oracle.plan_ref(qo, kv, base)
+    b = oracle.plan_ref(qo, kv, dataclasses_replace(base, decode_tile_q=16))
+    assert np.array_equal(a["items"], b["items"]) and a["worker_items"] == b["worker_items"]
+    assert (b["item_class"] == 0).all()
+
+
+def dataclasses_replace(p, **kw):
+    import dataclasses
+    return dataclasses.replace(p, **kw)
