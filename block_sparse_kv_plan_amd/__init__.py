@@ -22,7 +22,7 @@ import torch  # noqa: F401  (load order only)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsk.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_kv_plan_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python block_sparse_kv_plan_amd/build.py` "
                       "(or __graft_entry__.build()) -- there is no fallback path")
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -42,7 +42,7 @@ class Problem(ctypes.Structure):
                 ("tile_q", i32), ("tile_kv", i32), ("num_workers", i32), ("split_factor", i32),
                 ("min_chunk", i32), ("max_chunk", i32), ("item_overhead", i32), ("max_batch", i32),
                 ("max_items_per_worker", i32), ("max_slots", i32), ("max_merge", i32),
-                ("independent_kv_strides", i32)]
+                ("independent_kv_strides", i32), ("decode_tile_q", i32)]
 
 
 class PlanInfo(ctypes.Structure):

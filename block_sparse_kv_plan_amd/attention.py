@@ -29,7 +29,8 @@ def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE
                  page_size=16, causal=False, window=0, sink=0, rope_mode=ROPE_NONE, rope_theta=10000.0,
                  sm_scale=None, tile_q=TILE_DECODE, num_workers, tile_kv=None, split_factor=None,
                  min_chunk=None, max_chunk=0, item_overhead=0, max_batch, max_items_per_worker=None,
-                 max_slots=None, max_merge=None, fused_merge=0, independent_kv_strides=0) -> Problem:
+                 max_slots=None, max_merge=None, fused_merge=0, independent_kv_strides=0,
+                 decode_tile_q=0) -> Problem:
     d = DEFAULTS[tile_q]
     tile_kv = tile_kv if tile_kv is not None else max(d["tile_kv"], page_size if kv_mode == KV_PAGED else 1)
     kmax = max_items_per_worker if max_items_per_worker is not None else d["max_items_per_worker"]
@@ -49,6 +50,7 @@ def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE
     p.max_slots = max_slots if max_slots is not None else num_workers * kmax
     p.max_merge = max_merge if max_merge is not None else num_workers * kmax
     p.independent_kv_strides = independent_kv_strides
+    p.decode_tile_q = decode_tile_q
     return p
 
 

@@ -64,6 +64,8 @@ bsk_status check_problem(const bsk_problem* p) {
   if (p->fused_merge != 0 && p->fused_merge != 1) return fail(BSK_ERR_INVALID_ARG, "fused_merge must be 0 or 1");
   if (p->independent_kv_strides != 0 && p->independent_kv_strides != 1)
     return fail(BSK_ERR_INVALID_ARG, "independent_kv_strides must be 0 or 1");
+  if (p->decode_tile_q != 0 && (p->decode_tile_q != BSK_TILE_DECODE || p->tile_q != BSK_TILE_PREFILL))
+    return fail(BSK_ERR_INVALID_ARG, "decode_tile_q must be 0, or 16 with tile_q 128");
   if (p->window > 0 && p->sink < 0) return fail(BSK_ERR_INVALID_ARG, "sink must be >= 0");
   if (p->rope_mode < BSK_ROPE_NONE || p->rope_mode > BSK_ROPE_ABSOLUTE) return fail(BSK_ERR_INVALID_ARG, "rope_mode");
   if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
@@ -106,6 +108,7 @@ bsk::PlanParams plan_params(const bsk_problem& p) {
   q.causal = p.causal != 0;
   q.window = p.window > 0 ? p.window : 0;
   q.sink = p.window > 0 ? p.sink : 0;
+  q.decode_tile_q = p.decode_tile_q;
   return q;
 }
 

@@ -56,7 +56,8 @@ enum : int {
   IT_QLEN = 9,    // the request's query length
   IT_KVLEN = 10,  // the request's kv_len
   IT_KBASE = 11,  // the request's kv_indptr[r]: first page (paged) or token (dense) offset
-  ITEM_WORDS = 16,  // words 12..15 are zero
+  IT_CLASS = 12,  // tile class: 0 = the plan's tile_q, 1 = the decode tile (mixed launches)
+  ITEM_WORDS = 16,  // words 13..15 are zero
 };
 
 // merge record

@@ -77,11 +77,11 @@ Layout layout_for(int32_t W, int64_t n_items, int64_t n_merge, int64_t n_slots, 
 }
 
 struct Unit {
-  int32_t r, h, row_lo, row_hi, lo, hi, sink_hi;
+  int32_t r, h, row_lo, row_hi, lo, hi, sink_hi, cls;
 };
 
 struct Item {
-  int32_t r, h, row_lo, row_hi, kv_lo, kv_hi, slot;
+  int32_t r, h, row_lo, row_hi, kv_lo, kv_hi, slot, cls;
   int64_t cost;
 };
 
@@ -155,13 +155,17 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     const int32_t L = kv_len[r];
     if (Q == 0 || L == 0) continue;
     const int32_t rows = Q * g;
+    // two tile classes: a request whose rows fit one decode tile gets one decode-class unit
+    const bool small = p.decode_tile_q > 0 && rows <= p.decode_tile_q;
+    const int32_t tq = small ? p.decode_tile_q : p.tile_q;
     for (int32_t h = 0; h < p.num_kv_heads; ++h) {
-      for (int32_t t = 0; t < int32_t(ceil_div(rows, p.tile_q)); ++t) {
+      for (int32_t t = 0; t < int32_t(ceil_div(rows, tq)); ++t) {
         Unit u;
         u.r = r;
         u.h = h;
-        u.row_lo = t * p.tile_q;
-        u.row_hi = std::min(rows, (t + 1) * p.tile_q);
+        u.cls = small ? 1 : 0;
+        u.row_lo = t * tq;
+        u.row_hi = std::min(rows, (t + 1) * tq);
         const int32_t qpos_lo = L - Q + u.row_lo / g;
         const int32_t qpos_hi = L - Q + (u.row_hi - 1) / g;
         u.hi = p.causal ? std::min(L, qpos_hi + 1) : L;
@@ -210,6 +214,7 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
       it.kv_lo = chunks[c].first;
       it.kv_hi = chunks[c].second;
       it.slot = split ? int32_t(first + int64_t(c)) : -1;
+      it.cls = u.cls;
       it.cost = int64_t(it.kv_hi - it.kv_lo) + p.item_overhead;
       items.push_back(it);
     }
@@ -316,6 +321,7 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     rec[IT_QLEN] = qo_indptr[it.r + 1] - qo_indptr[it.r];
     rec[IT_KVLEN] = kv_len[it.r];
     rec[IT_KBASE] = kv_indptr[it.r];
+    rec[IT_CLASS] = it.cls;
   }
   for (size_t m = 0; m < merges.size(); ++m) {
     int32_t* rec = buf + L.off_merge + int64_t(m) * MERGE_WORDS;

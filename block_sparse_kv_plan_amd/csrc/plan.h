@@ -24,6 +24,7 @@ struct PlanParams {
   bool causal = false;
   int32_t window = 0;
   int32_t sink = 0;
+  int32_t decode_tile_q = 0;  // > 0: requests with qo_len * g <= decode_tile_q get one decode-class tile
 };
 
 struct PlanStats {

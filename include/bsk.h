@@ -113,6 +113,13 @@ typedef struct bsk_problem {
      per key and reach V through the K-to-V pointer distance; 1 -- always
      use the kernels that address K and V with their own strides */
   int32_t independent_kv_strides;
+  /* Two tile classes in one launch ([FI-PR5329, code analysis 1]): 0 (off)
+     or BSK_TILE_DECODE with tile_q = BSK_TILE_PREFILL -- requests whose
+     qo_len * g rows fit one 16-row tile are planned as decode-class items,
+     all others as 128-row items, balanced over the same workers, and
+     bsk_run_prefill runs both classes in one persistent launch (bf16,
+     paged, no RoPE). */
+  int32_t decode_tile_q;
 } bsk_problem;
 
 /* Filled by bsk_plan; passed unchanged to run/merge. */

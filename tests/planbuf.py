@@ -3,7 +3,7 @@ block_sparse_kv_plan_amd/csrc/layout.h).  Test infrastructure only."""
 import numpy as np
 
 HDR_WORDS = 16
-ITEM_WORDS = 16  # 8 plan fields, 4 copied request fields (q0, qo_len, kv_len, kv_indptr), 4 zero
+ITEM_WORDS = 16  # 8 plan fields, 4 copied request fields (q0, qo_len, kv_len, kv_indptr), tile class, 3 zero
 MERGE_WORDS = 8
 
 
@@ -19,7 +19,8 @@ def decode(buf) -> dict:
         "tile_q": tile_q, "max_kv_len": int(w[12]), "max_qo_len": int(w[13]),
         "worker_items": [items[wptr[k]:wptr[k + 1], :8] for k in range(W)],
         "worker_req": [items[wptr[k]:wptr[k + 1], 8:12] for k in range(W)],
-        "item_pad": items[:, 12:],
+        "worker_class": [items[wptr[k]:wptr[k + 1], 12] for k in range(W)],
+        "item_pad": items[:, 13:],
         "merge": merge,
         "qo_indptr": w[off_qo:off_qo + batch + 1], "kv_len": w[off_kvlen:off_kvlen + batch],
         "kv_indptr": w[off_kvind:off_kvind + batch + 1],

@@ -45,7 +45,7 @@ def ref_params(problem):
         min_chunk=problem.min_chunk, max_chunk=effective_max_chunk(problem), item_overhead=problem.item_overhead,
         max_items_per_worker=problem.max_items_per_worker, max_slots=problem.max_slots,
         max_merge=problem.max_merge, causal=bool(problem.causal), window=max(problem.window, 0),
-        sink=problem.sink if problem.window > 0 else 0)
+        sink=problem.sink if problem.window > 0 else 0, decode_tile_q=problem.decode_tile_q)
 
 
 def assert_same_plan(problem, qo_len, kv_len):
@@ -65,6 +65,8 @@ def assert_same_plan(problem, qo_len, kv_len):
         req = np.stack([qo_indptr[r], qo_indptr[r + 1] - qo_indptr[r], np.asarray(kv_len)[r], kv_indptr[r]], axis=1) \
             if len(r) else np.zeros((0, 4), dtype=np.int64)
         assert np.array_equal(got["worker_req"][w].astype(np.int64), req.astype(np.int64)), f"worker {w} request fields"
+        assert np.array_equal(got["worker_class"][w].astype(np.int64), ref["item_class"][ids] if ids else
+                              np.zeros(0, dtype=np.int64)), f"worker {w} tile classes"
     assert (got["item_pad"] == 0).all()
     assert np.array_equal(got["merge"][:, :6].astype(np.int64), ref["merge"])
     assert info.max_load == int(ref["load"].max()) if len(ref["items"]) else True
@@ -137,7 +139,31 @@ def test_random_plans(seed):
                        max_items_per_worker=4096, max_slots=1 << 20, max_merge=1 << 20)
     if p.max_chunk and p.max_chunk < p.min_chunk:
         p.max_chunk = p.min_chunk
+    if tile_q == bsk.TILE_PREFILL and rng.integers(0, 2):
+        p.decode_tile_q = bsk.TILE_DECODE  # mixed launch: two tile classes
     assert_same_plan(p, qo, kv)
+
+
+def test_mixed_plan_classes():
+    """A decode-heavy batch with a few prefill requests: small requests become decode-class items
+    (one per kv head and chunk), large ones 128-row items, and the record's class word says which."""
+    qo = [1] * 40 + [300, 1, 2, 64, 500] + [1] * 20
+    kv = [2000 + 37 * i for i in range(len(qo))]
+    kv[40], kv[43], kv[44] = 300, 900, 500
+    p = decode_problem(32, 8, 128, 64, tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE, causal=True,
+                       split_factor=2, min_chunk=256, max_items_per_worker=4096, max_slots=1 << 20, max_merge=1 << 20)
+    info, ref = assert_same_plan(p, qo, kv)
+    cls = ref["item_class"]
+    assert set(np.unique(cls)) == {0, 1}
+    rows = np.asarray(ref["items"])[:, 3] - np.asarray(ref["items"])[:, 2]
+    assert rows[cls == 1].max() <= bsk.TILE_DECODE
+    assert rows[cls == 0].max() <= bsk.TILE_PREFILL
+
+
+def test_mixed_class_requires_prefill_tile():
+    with pytest.raises(bsk.BskError):
+        p = decode_problem(8, 2, 64, 4, tile_q=bsk.TILE_PREFILL_256, decode_tile_q=bsk.TILE_DECODE)
+        cpp_plan(p, [1], [10])
 
 
 def test_capacity_and_invalid_errors():
