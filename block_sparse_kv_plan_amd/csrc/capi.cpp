@@ -66,6 +66,8 @@ bsk_status check_problem(const bsk_problem* p) {
     return fail(BSK_ERR_INVALID_ARG, "independent_kv_strides must be 0 or 1");
   if (p->decode_tile_q != 0 && (p->decode_tile_q != BSK_TILE_DECODE || p->tile_q != BSK_TILE_PREFILL))
     return fail(BSK_ERR_INVALID_ARG, "decode_tile_q must be 0, or 16 with tile_q 128");
+  if (p->decode_tile_q != 0 && p->kv_mode != BSK_KV_PAGED)
+    return fail(BSK_ERR_UNSUPPORTED, "the mixed launch is built for the paged layout only");
   if (p->window > 0 && p->sink < 0) return fail(BSK_ERR_INVALID_ARG, "sink must be >= 0");
   if (p->rope_mode < BSK_ROPE_NONE || p->rope_mode > BSK_ROPE_ABSOLUTE) return fail(BSK_ERR_INVALID_ARG, "rope_mode");
   if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
@@ -220,7 +222,10 @@ bsk_status bsk_device_workers(const bsk_problem* problem, int32_t* num_workers) 
     threads = bsk::decode_threads();
   } else if (is_prefill_tile(problem->tile_q)) {
     if (problem->dtype == BSK_DTYPE_BF16 && problem->rope_mode == BSK_ROPE_NONE)
-      fn = bsk::prefill_kernel_ptr(problem->head_dim, dense, problem->tile_q, problem->independent_kv_strides == 0);
+      fn = problem->decode_tile_q != 0
+               ? bsk::mixed_kernel_ptr(problem->head_dim, problem->independent_kv_strides == 0)
+               : bsk::prefill_kernel_ptr(problem->head_dim, dense, problem->tile_q,
+                                         problem->independent_kv_strides == 0);
     threads = bsk::prefill_threads();
   } else {
     return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16, 128 or 256");
@@ -330,8 +335,12 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
       return fail(BSK_ERR_INVALID_ARG, "head / token strides too large for the prefill kernel's 32-bit row offsets");
   }
   const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
-  hipError_t e = bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, problem->tile_q,
-                                     same_kv(*problem, *t), a, info->num_workers, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      problem->decode_tile_q != 0
+          ? bsk::launch_mixed(problem->head_dim, same_kv(*problem, *t), a, info->num_workers,
+                              static_cast<hipStream_t>(stream))
+          : bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, problem->tile_q,
+                                same_kv(*problem, *t), a, info->num_workers, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return BSK_OK;
 }

@@ -1,0 +1,451 @@
+// Small-tile work item (16 query rows): the body of the small-tile persistent
+// attention kernel, shared with the mixed launch.
+//
+// Serves decode -- query length 1, one row per q head of a GQA group, the
+// HBM-bound case of the FlashInfer 0.6 wiki ("Kernel types": Decode) -- and
+// short multi-token queries.  One workgroup is one persistent worker: it
+// walks its item list from the int workspace (FlashInfer paper summary,
+// "Research methodology" 3: the CPU plan cached on the GPU drives a fixed
+// launch).  Per item:
+//
+//   * the item's page ids are staged in LDS (FlashInfer 0.6 wiki,
+//     "Architecture" 1: page indices prefetched into shared memory);
+//   * keys are walked in 16-key blocks aligned to multiples of 16, so with
+//     pages of >= 16 keys a block lies in one page and needs one page id;
+//     the four waves take interleaved blocks and keep the next block's
+//     loads in flight while consuming the current one;
+//   * S^T = K Q^T on MFMA with the 16 keys on the M side and the (up to 16)
+//     query rows on the N side: each lane ends up owning one query row, so
+//     the row max / sum take two cross-lane steps;
+//   * online softmax in base 2 (log2 e folded into the scale); the output
+//     accumulator is rescaled only when a row's running max grows by more
+//     than 2^8 (values stay exact: numerator and denominator share the max);
+//   * O^T += V^T P^T on bf16 MFMA without any LDS transpose: each lane loads
+//     whole 16-byte pieces of four V rows (fully coalesced), and the MFMA's
+//     key index k = 4j+e is mapped to key 4e+j so that the A operand is a
+//     repack of those registers; the K rows are loaded in the matching
+//     transposed order (lane row m holds key 4(m%4) + m/4) so the logits
+//     land in the lanes that need them as the B operand;
+//   * the four waves' states are combined through LDS; a single-chunk item
+//     writes O and LSE, a chunk of a split unit writes its partial state.
+//
+// f32 inputs use the 16x16x4 f32 MFMA (one k element per lane), which
+// reads V straight from memory.
+//
+// Fused RoPE (bf16): q and every key are rotated in fp32 with a cos/sin
+// table (the cache holds K unrotated), then split into bf16 hi + lo parts so
+// the MFMA logits keep ~16 significant bits: S = Kh.Qh + Kh.Ql + Kl.Qh.
+
+#pragma once
+
+#include "device.h"
+
+namespace bsk {
+
+constexpr int kDecRows = 16;
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr float kRescaleSlack = 8.f;  // log2 units: rescale only when the max grows by > 2^8
+
+enum : int { ROPE_NONE = 0, ROPE_STREAMING = 1, ROPE_ABSOLUTE = 2 };
+
+// Rotate-half RoPE on a lane's fragment pair: lo holds elements k..k+7 of
+// the first half, hi the matching k+D/2.. elements; cs points at the (cos,
+// sin) pairs of k..k+7 for the position.
+__device__ __forceinline__ void rope8(float* lo, float* hi, const float* __restrict__ cs) {
+  const float4* c4 = reinterpret_cast<const float4*>(cs);
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const float4 t = c4[e2];  // cos_e, sin_e, cos_e+1, sin_e+1
+    const int e = 2 * e2;
+    float x = lo[e], y = hi[e];
+    lo[e] = x * t.x - y * t.y;
+    hi[e] = y * t.x + x * t.y;
+    x = lo[e + 1];
+    y = hi[e + 1];
+    lo[e + 1] = x * t.z - y * t.w;
+    hi[e + 1] = y * t.z + x * t.w;
+  }
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const bf16x8& v, float* f) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf16_lo(u[e]);
+    f[2 * e + 1] = bf16_hi(u[e]);
+  }
+}
+
+// f (8 floats) -> hi = bf16(f), lo = bf16(f - hi)
+__device__ __forceinline__ void split_bf16x8(const float* f, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h0 = f32_to_bf16_bits(f[2 * e]);
+    const uint32_t h1 = f32_to_bf16_bits(f[2 * e + 1]);
+    h[e] = h0 | (h1 << 16);
+    l[e] = pack_bf16x2(f[2 * e] - __uint_as_float(h0 << 16), f[2 * e + 1] - __uint_as_float(h1 << 16));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// Element e of four 8-element pieces (a, b, c, d), as an MFMA k-quad.
+__device__ __forceinline__ i16x4 gather_e(const u32x4& a, const u32x4& b, const u32x4& c, const u32x4& d, int e) {
+  const int w = e >> 1;
+  // v_perm_b32 selector: low halves (bytes 1:0 of each source) or high halves (bytes 3:2)
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  u32x2 r;
+  r[0] = __builtin_amdgcn_perm(b[w], a[w], sel);
+  r[1] = __builtin_amdgcn_perm(d[w], c[w], sel);
+  return __builtin_bit_cast(i16x4, r);
+}
+
+// LDS of one workgroup for a small-tile item: the four waves' accumulators, maxima and sums
+// for the combine step (rows padded by 4 floats).
+template <int D>
+struct DecodeSmem {
+  float acc[kDecWaves * 16 * (D + 4)];
+  float m[kDecWaves][16];
+  float l[kDecWaves][16];
+};
+
+// SAME: K and V share page/head/token strides, so one offset serves both tensors.
+template <typename T, int D, bool DENSE, int ROPE, bool SAME>
+__device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __restrict__ rec, DecodeSmem<D>& sm,
+                                            int32_t* s_pages, int* s_last, int part_rows) {
+  constexpr bool BF = __is_same(T, __bf16);
+  constexpr int NKS = BF ? D / 32 : D / 4;  // MFMA k-steps over d for the logits
+  constexpr int NACC = BF ? 8 : D / 16;     // f32x4 accumulators per lane
+  constexpr int HALF_KS = D / 64;           // bf16 k-step offset of the rotate-half partner
+  constexpr int CHUNKS = D / 8;             // 16-byte pieces per bf16 row
+  constexpr int AROW = D + 4;               // floats per row of the combine buffer
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(BF || ROPE == ROPE_NONE, "fused RoPE is built for bf16 only");
+
+  float* s_acc = sm.acc;
+  float (&s_m)[kDecWaves][16] = sm.m;
+  float (&s_l)[kDecWaves][16] = sm.l;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int n = lane & 15;  // MFMA N index: this lane's query row
+  const int j = lane >> 4;  // lane group
+  // key row (within a 16-key block) this lane feeds to the logits MFMA
+  const int kkey = BF ? 4 * (n & 3) + (n >> 2) : n;
+
+  const T* __restrict__ Qp = static_cast<const T*>(a.q);
+  const T* __restrict__ Kp = static_cast<const T*>(a.k);
+  const T* __restrict__ Vp = static_cast<const T*>(a.v);
+  const int g = a.group;
+  const bool block_in_page = DENSE || a.page_shift >= 4;  // an aligned 16-key block never crosses a page
+
+  {
+    const int r = rec[IT_R], h = rec[IT_H];
+    const int row_lo = rec[IT_ROW_LO], row_hi = rec[IT_ROW_HI];
+    const int kv_lo = rec[IT_KV_LO], kv_hi = rec[IT_KV_HI];
+    const int slot = rec[IT_SLOT];
+    const int q0 = rec[IT_Q0];
+    const int qlen = rec[IT_QLEN];
+    const int L = rec[IT_KVLEN];
+    const int kbase = rec[IT_KBASE];
+    (void)r;
+
+    if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, kDecThreads);
+    __syncthreads();
+
+    // ---- this lane's query row and its q fragment (MFMA B operand)
+    const int rho = row_lo + n;
+    const bool row_ok = rho < row_hi;
+    const int qi = row_ok ? rho / g : 0;
+    const int qu = row_ok ? rho % g : 0;
+    const int qpos = L - qlen + qi;
+    const T* qrow = Qp + int64_t(q0 + qi) * a.q_st + int64_t(h * g + qu) * a.q_sh;
+
+    // RoPE positions: streaming = rank within the visible set (sinks, then the window)
+    int lo_w = 0, n_s = 0;
+    if constexpr (ROPE == ROPE_STREAMING) {
+      lo_w = a.window > 0 ? max(0, qpos - a.window + 1) : 0;
+      n_s = a.window > 0 ? min(a.sink, lo_w) : 0;
+    }
+
+    bf16x8 qh[BF ? NKS : 1], ql[BF && ROPE != ROPE_NONE ? NKS : 1];
+    float qf[BF ? 1 : NKS];
+    if constexpr (BF) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        qh[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 8 * (4 * s + j)) : bf16x8{};
+      }
+      if constexpr (ROPE != ROPE_NONE) {
+        int pq = ROPE == ROPE_STREAMING ? n_s + (qpos - lo_w) : qpos;
+        pq = min(max(pq, 0), a.rope_n_pos - 1);
+#pragma unroll
+        for (int s = 0; s < HALF_KS; ++s) {
+          float lo[8], hi[8];
+          unpack_bf16x8(qh[s], lo);
+          unpack_bf16x8(qh[s + HALF_KS], hi);
+          rope8(lo, hi, a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2);
+          split_bf16x8(lo, qh[s], ql[s]);
+          split_bf16x8(hi, qh[s + HALF_KS], ql[s + HALF_KS]);
+        }
+        if (!row_ok) {
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) qh[s] = ql[s] = bf16x8{};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NKS; s += 4) {
+        const float4 x = row_ok ? *reinterpret_cast<const float4*>(qrow + j * (D / 4) + s) : float4{0, 0, 0, 0};
+        qf[s] = x.x;
+        qf[s + 1] = x.y;
+        qf[s + 2] = x.z;
+        qf[s + 3] = x.w;
+      }
+    }
+
+    const RowMask rm = row_mask(row_ok, qpos, kv_hi, a.causal, a.window, a.sink);
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[NACC];
+#pragma unroll
+    for (int e = 0; e < NACC; ++e) acc[e] = f32x4{0, 0, 0, 0};
+
+    const int blk0 = kv_lo >> 4;
+    const int nblk = ((kv_hi - 1) >> 4) - blk0 + 1;
+    const int kmin = kv_lo, kmax = kv_hi - 1;
+
+    // element offsets of key t of kv head h (K and V strides may differ)
+    auto key_offsets = [&](int t, int64_t& ko, int64_t& vo) {
+      ko = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
+      if constexpr (SAME)
+        vo = ko;
+      else
+        vo = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
+    };
+
+    // masked, scaled logits -> probabilities; online-softmax state update
+    auto softmax_update = [&](float* sv, float* p) {
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = wave_max_xor16_32(bm);
+      const bool grow = bm > m_run + kRescaleSlack || (m_run == -INFINITY && bm > -INFINITY);
+      if (__any(grow)) {  // wave-uniform: rescale only when some row's max jumps
+        const float m_new = grow ? bm : m_run;
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < NACC; ++e) acc[e] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    };
+
+    if constexpr (BF) {
+      // K: this lane's key row kkey, pieces 4s + j.  V: keys 4i + j (i = 0..3), piece n % CHUNKS.
+      auto load_block = [&](int b, bf16x8* kf, u32x4* vf) {
+        const int tb = (blk0 + b) << 4;
+        if (block_in_page) {
+          const int t0 = min(max(tb, kmin), kmax);
+          int64_t kb, vb;
+          key_offsets(t0, kb, vb);  // one page id serves the whole block
+          const int tk = min(max(tb + kkey, kmin), kmax);
+#pragma unroll
+          for (int s = 0; s < NKS; ++s)
+            kf[s] = *reinterpret_cast<const bf16x8*>(Kp + kb + int64_t(tk - t0) * a.k_st + 8 * (4 * s + j));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tv = min(max(tb + 4 * i + j, kmin), kmax);
+            vf[i] = *reinterpret_cast<const u32x4*>(Vp + vb + int64_t(tv - t0) * a.v_st + 8 * (n % CHUNKS));
+          }
+        } else {
+          int64_t ko, vo;
+          key_offsets(min(max(tb + kkey, kmin), kmax), ko, vo);
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(Kp + ko + 8 * (4 * s + j));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            key_offsets(min(max(tb + 4 * i + j, kmin), kmax), ko, vo);
+            vf[i] = *reinterpret_cast<const u32x4*>(Vp + vo + 8 * (n % CHUNKS));
+          }
+        }
+      };
+
+      auto compute_block = [&](int b, bf16x8* kf, const u32x4* vf) {
+        const int tb = (blk0 + b) << 4;
+        f32x4 st = {0, 0, 0, 0};
+        if constexpr (ROPE == ROPE_NONE) {
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
+        } else {
+          const int tk = min(max(tb + kkey, kmin), kmax);
+          int pk = ROPE == ROPE_STREAMING ? (tk < n_s ? tk : n_s + (tk - lo_w)) : tk;
+          pk = min(max(pk, 0), a.rope_n_pos - 1);
+          bf16x8 kl[NKS];
+#pragma unroll
+          for (int s = 0; s < HALF_KS; ++s) {
+            float lo[8], hi[8];
+            unpack_bf16x8(kf[s], lo);
+            unpack_bf16x8(kf[s + HALF_KS], hi);
+            rope8(lo, hi, a.rope + (int64_t(pk) * (D / 2) + 8 * (4 * s + j)) * 2);
+            split_bf16x8(lo, kf[s], kl[s]);
+            split_bf16x8(hi, kf[s + HALF_KS], kl[s + HALF_KS]);
+          }
+#pragma unroll
+          for (int s = 0; s < NKS; ++s) {
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], ql[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[s], qh[s], st, 0, 0, 0);
+          }
+        }
+        // st[i]: logit of key tb + 4i + j for query row n
+        float sv[4], p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb + 4 * i + j;
+          sv[i] = (row_sees(rm, t) & (t >= kv_lo)) ? st[i] * a.scale_log2 : -INFINITY;
+        }
+        softmax_update(sv, p);
+        u32x2 pw;
+        pw[0] = pack_bf16x2(p[0], p[1]);
+        pw[1] = pack_bf16x2(p[2], p[3]);
+        const i16x4 pb = __builtin_bit_cast(i16x4, pw);
+        // A operand e: element e of this lane's four V pieces = V[key 4i+j][d = 8*(n%CHUNKS) + e]
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gather_e(vf[0], vf[1], vf[2], vf[3], e), pb, acc[e],
+                                                              0, 0, 0);
+      };
+
+      // two register sets: the next block's loads are in flight while the current one is consumed
+      bf16x8 ka[NKS], kb2[NKS];
+      u32x4 va[4], vb2[4];
+      int b = wave;
+      if (b < nblk) load_block(b, ka, va);
+      for (; b < nblk; b += 2 * kDecWaves) {
+        const int b1 = b + kDecWaves;
+        if (b1 < nblk) load_block(b1, kb2, vb2);
+        compute_block(b, ka, va);
+        if (b1 >= nblk) break;
+        const int b2 = b1 + kDecWaves;
+        if (b2 < nblk) load_block(b2, ka, va);
+        compute_block(b1, kb2, vb2);
+      }
+    } else {
+      for (int b = wave; b < nblk; b += kDecWaves) {
+        const int tb = (blk0 + b) << 4;
+        int64_t ko, vo;
+        key_offsets(min(max(tb + n, kmin), kmax), ko, vo);
+        float kf[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; s += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(Kp + ko + j * (D / 4) + s);
+          kf[s] = x.x;
+          kf[s + 1] = x.y;
+          kf[s + 2] = x.z;
+          kf[s + 3] = x.w;
+        }
+        f32x4 st = {0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], qf[s], st, 0, 0, 0);
+        // st[i]: logit of key tb + 4j + i
+        float sv[4], p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb + 4 * j + i;
+          sv[i] = (row_sees(rm, t) & (t >= kv_lo)) ? st[i] * a.scale_log2 : -INFINITY;
+        }
+        softmax_update(sv, p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          key_offsets(min(max(tb + 4 * j + i, kmin), kmax), ko, vo);
+#pragma unroll
+          for (int db = 0; db < NACC; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(static_cast<float>(Vp[vo + 16 * db + n]), p[i], acc[db],
+                                                           0, 0, 0);
+        }
+      }
+    }
+
+    // ---- combine the four waves' states through LDS (each lane owns query row n)
+    l_run = wave_sum_xor16_32(l_run);
+    if (j == 0) {
+      s_m[wave][n] = m_run;
+      s_l[wave][n] = l_run;
+    }
+    __syncthreads();
+    {
+      const float M = fmaxf(fmaxf(s_m[0][n], s_m[1][n]), fmaxf(s_m[2][n], s_m[3][n]));
+      const float my = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      float* crow = s_acc + (wave * 16 + n) * AROW;
+      if constexpr (BF) {
+        // acc[e][i] holds column 8 * (4j + i) + e; with D = 64 lane groups j >= 2 repeat j - 2
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * j + i;
+          if (c < CHUNKS) {
+            *reinterpret_cast<float4*>(crow + 8 * c) =
+                float4{acc[0][i] * my, acc[1][i] * my, acc[2][i] * my, acc[3][i] * my};
+            *reinterpret_cast<float4*>(crow + 8 * c + 4) =
+                float4{acc[4][i] * my, acc[5][i] * my, acc[6][i] * my, acc[7][i] * my};
+          }
+        }
+      } else {
+        // acc[db][i] holds column 16 db + 4j + i
+#pragma unroll
+        for (int db = 0; db < NACC; ++db)
+          *reinterpret_cast<float4*>(crow + 16 * db + 4 * j) =
+              float4{acc[db][0] * my, acc[db][1] * my, acc[db][2] * my, acc[db][3] * my};
+      }
+    }
+    __syncthreads();
+    const int nrows = row_hi - row_lo;
+    for (int e = tid; e < nrows * (D / 4); e += kDecThreads) {
+      const int rr = e / (D / 4);
+      const int c4 = (e % (D / 4)) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+      float Lsum = 0.f;
+      float4 o = {0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        if (s_m[w][rr] != -INFINITY) Lsum += s_l[w][rr] * __builtin_amdgcn_exp2f(s_m[w][rr] - M);
+        const float4 x = *reinterpret_cast<const float4*>(s_acc + (w * 16 + rr) * AROW + c4);
+        o.x += x.x;
+        o.y += x.y;
+        o.z += x.z;
+        o.w += x.w;
+      }
+      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      o.x *= inv;
+      o.y *= inv;
+      o.z *= inv;
+      o.w *= inv;
+      const float lse = Lsum > 0.f ? (M + __log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+      const int row = row_lo + rr;
+      if (slot < 0) {
+        const int tok = q0 + row / g;
+        const int qhd = h * g + row % g;
+        const int64_t oo = int64_t(tok) * a.o_st + int64_t(qhd) * a.o_sh + c4;
+        if (a.out_bf16) {
+          uint2 pk2 = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+          *reinterpret_cast<uint2*>(static_cast<__bf16*>(a.out) + oo) = pk2;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oo) = o;
+        }
+        if (c4 == 0) a.lse[int64_t(tok) * a.lse_st + qhd] = lse;
+      } else {
+        *reinterpret_cast<float4*>(a.part_o + (int64_t(slot) * part_rows + rr) * D + c4) = o;
+        if (c4 == 0) a.part_lse[int64_t(slot) * part_rows + rr] = lse;
+      }
+    }
+    if (slot >= 0 && a.fused_merge) finish_split_chunk<D>(a, slot, tid, kDecThreads, s_last);
+    __syncthreads();
+  }
+}
+
+}  // namespace bsk

@@ -17,6 +17,9 @@ hipError_t launch_prefill(int head_dim, bool dense, int tile_q, bool same, const
 const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q, bool same);
 int prefill_threads();
 
+hipError_t launch_mixed(int head_dim, bool same, const AttnArgs& a, int grid, hipStream_t stream);
+const void* mixed_kernel_ptr(int head_dim, bool same);
+
 hipError_t launch_rope_apply(int head_dim, const RopeApplyArgs& a, int max_visible, hipStream_t stream);
 hipError_t launch_append(int dtype, int head_dim, const AppendArgs& a, hipStream_t stream);
 

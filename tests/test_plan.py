@@ -160,10 +160,16 @@ def test_mixed_plan_classes():
     assert rows[cls == 0].max() <= bsk.TILE_PREFILL
 
 
-def test_mixed_class_requires_prefill_tile():
+def test_mixed_class_requires_prefill_tile_and_paged_kv():
+    p = decode_problem(8, 2, 64, 4, tile_q=bsk.TILE_PREFILL_256, decode_tile_q=bsk.TILE_DECODE)
     with pytest.raises(bsk.BskError):
-        p = decode_problem(8, 2, 64, 4, tile_q=bsk.TILE_PREFILL_256, decode_tile_q=bsk.TILE_DECODE)
         cpp_plan(p, [1], [10])
+    p = decode_problem(8, 2, 64, 4, tile_q=bsk.TILE_PREFILL, decode_tile_q=8)
+    with pytest.raises(bsk.BskError):
+        cpp_plan(p, [1], [10])
+    p = decode_problem(8, 2, 64, 4, tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE, kv_mode=bsk.KV_DENSE)
+    with pytest.raises(bsk.BskError):
+        cpp_plan(p, [1], [10], kv_indptr=np.array([0, 10], dtype=np.int32))
 
 
 def test_capacity_and_invalid_errors():

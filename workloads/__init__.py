@@ -334,6 +334,37 @@ def shared_prefix(seed: int = 4, branches: int = 64, prefix_len: int = 16384,
     return Composable(prefix=prefix, suffix=suffix)
 
 
+def mixed_lengths(seed: int = 6, decode: int = 64, prefill: int = 4, d_lo: int = 512, d_hi: int = 8192,
+                  q_lo: int = 256, q_hi: int = 2048, p_lo: int = 0, p_hi: int = 2048):
+    """Continuous batching: `decode` one-token requests with lognormal [d_lo, d_hi] kv lengths and
+    `prefill` chunk requests (lognormal [q_lo, q_hi] new tokens after a uniform [p_lo, p_hi] cached
+    prefix), the prefill requests spread evenly through the batch."""
+    r = rng_for(seed, LEN_STREAM)
+    dkv = lognormal_lengths(r, decode, d_lo, d_hi)
+    pq = lognormal_lengths(r, prefill, q_lo, q_hi)
+    pp = uniform_lengths(r, prefill, p_lo, p_hi)
+    qo = np.ones(decode + prefill, dtype=np.int64)
+    kv = np.zeros(decode + prefill, dtype=np.int64)
+    at = set(int(i) for i in np.linspace(0, decode + prefill - 1, prefill).round()) if prefill else set()
+    di = pi = 0
+    for i in range(decode + prefill):
+        if i in at:
+            qo[i], kv[i] = pq[pi], pp[pi] + pq[pi]
+            pi += 1
+        else:
+            kv[i] = dkv[di]
+            di += 1
+    return qo, kv
+
+
+def mixed(seed: int = 6, decode: int = 64, prefill: int = 4) -> Batch:
+    """Mixed decode + prefill batch of one Llama-3-8B-shaped layer: 32 q / 8 kv heads, d 128, bf16,
+    page_size 16, causal (see mixed_lengths)."""
+    qo, kv = mixed_lengths(seed, decode, prefill)
+    return paged_batch(name="mixed_decode_prefill_bf16", seed=seed, kv_len=kv, qo_len=qo, num_qo_heads=32,
+                       num_kv_heads=8, head_dim=128, page_size=16, dtype=BF16, causal=True)
+
+
 def streaming_rope_decode_lengths(seed: int = 5, batch: int = 8, lo: int = 32768, hi: int = 131072):
     kv = uniform_lengths(rng_for(seed, LEN_STREAM), batch, lo, hi)
     return np.ones(batch, dtype=np.int64), kv
