@@ -15,8 +15,9 @@ out + lse + page ids) per wall-clock step, in TB/s.
 Also reported (same JSON line): the decode kernel's roofline (HIP events on
 its own stream), the fp64 oracle timed on a bounded sample of the same
 batch on the host cores, and secondary measurements of the ragged causal
-prefill (TFLOP/s vs bf16 MFMA peak), the shared-prefix composable format
-and the fused-RoPE streaming decode.
+prefill (TFLOP/s vs bf16 MFMA peak), the shared-prefix composable format,
+the fused-RoPE streaming decode and a mixed decode + prefill batch in one
+launch.
 """
 from __future__ import annotations
 
@@ -41,7 +42,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("decode.hip", "device.h", "args.h", "layout.h"):
+    for f in ("decode.hip", "decode_item.h", "device.h", "args.h", "layout.h"):
         with open(os.path.join(ROOT, "block_sparse_kv_plan_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -203,6 +204,70 @@ def load_traffic(name, launches_bytes):
     return d.get("hbm_bytes_per_launch")
 
 
+def mixed_leg(device, reps):
+    """GPU time of one mixed batch (64 decode requests and 4 prefill chunks): the mixed launch
+    (both tile classes in one persistent kernel, then the state merge) against the decode
+    kernel over the decode requests followed by the prefill kernel over the prefill requests
+    (each with its merge).  Plans are built once; HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import block_sparse_kv_plan_amd as bsk
+    import workloads as W
+    from block_sparse_kv_plan_amd.attention import tensors_for
+    from tests.gpu_util import upload
+    b = W.mixed()
+    dec = b.qo_len == 1
+    parts = {"mixed": (b, dict(tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE))}
+    for name, sel, tq in (("decode", dec, bsk.TILE_DECODE), ("prefill", ~dec, bsk.TILE_PREFILL)):
+        sub = W.paged_batch(name=f"mixed_{name}_part", seed=7, kv_len=b.kv_len[sel], qo_len=b.qo_len[sel],
+                            num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                            page_size=b.page_size, dtype=b.dtype, causal=True)
+        parts[name] = (sub, dict(tile_q=tq))
+    stream = torch.cuda.current_stream()
+    runs = {}
+    for name, (bb, kw) in parts.items():
+        tq = kw.pop("tile_q")
+        attn = make_attention(bb, tq, 0, device, **kw)
+        d = upload(bb, device=device)
+        T = int(bb.qo_indptr[-1])
+        out = torch.empty((T, bb.num_qo_heads, bb.head_dim), dtype=torch.float32, device=device)
+        lse = torch.empty((T, bb.num_qo_heads), dtype=torch.float32, device=device)
+        t = tensors_for(attn.problem, d["q"], d["k"], d["v"], out, lse, page_indices=d["pages"])
+        attn.plan(bb.qo_indptr, bb.kv_len, d["kv_indptr"], stream=stream)
+        runs[name] = (attn, t, d, out, lse)
+
+    def go(names):
+        for n in names:
+            attn, t = runs[n][0], runs[n][1]
+            attn.run(t, stream=stream)
+
+    res = {}
+    for label, names in (("one_launch", ["mixed"]), ("two_launches", ["decode", "prefill"])):
+        for _ in range(3):
+            go(names)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e in evs:
+            e[0].record(stream)
+            go(names)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        res[label] = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e3
+    info = runs["mixed"][0].info
+    flops, _ = prefill_flops(parts["prefill"][0])
+    nbytes = decode_bytes(parts["decode"][0])
+    return {
+        "workload": "mixed_decode_prefill_bf16: 64 decode requests (kv lognormal [512,8192]) + 4 prefill chunks "
+                    "(lognormal [256,2048] new tokens after uniform [0,2048] cached), 32q/8kv, d128, page 16",
+        "one_launch_us": round(res["one_launch"], 2), "two_launches_us": round(res["two_launches"], 2),
+        "speedup": round(res["two_launches"] / res["one_launch"], 3),
+        "mixed_items": info.num_items, "mixed_workers": info.num_workers, "mixed_merges": info.num_merge,
+        "decode_part_bytes": nbytes, "prefill_part_flops": flops,
+        "note": "kernel + merge GPU time per batch, plans built once; the parts of the two-launch run are "
+                "separate batches of the same lengths and shapes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,7 +276,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling aid: run just this workload (decode|prefill|append|strides|composable|rope)")
+                    help="profiling aid: run just this workload (decode|prefill|append|strides|composable|rope|mixed)")
     ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
                     help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
     ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
@@ -475,6 +540,11 @@ def main():
             "gpu_us_per_step": round(gpu * 1e6, 1), "wall_us_per_step": round(wall * 1e6, 1),
             "effective_gbs": round((pb + sb) / gpu / 1e9, 1), "algorithmic_bytes": pb + sb}
         del pre, suf
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "mixed"):
+        log("mixed: 64 decode requests + 4 prefill chunks, one mixed launch vs decode + prefill launches")
+        secondary["mixed_batch"] = mixed_leg(device, reps=max(10, args.steps // 2))
         torch.cuda.empty_cache()
 
     if result:
