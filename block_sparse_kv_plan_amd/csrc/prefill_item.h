@@ -166,7 +166,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
         qf[nb][s] = row_ok[nb] ? *reinterpret_cast<const bf16x8*>(qrow + 8 * (4 * s + j)) : bf16x8{};
     }
     // the wave's query-position range (rows past row_hi excluded), for the mask-free test
-    const int wrow0 = row_lo + WROWS * wave;
+    const int wrow0 = row_lo + WROWS * wave_u;  // wave-uniform: the tile tests below stay scalar
     const int wrow1 = min(row_hi, wrow0 + WROWS) - 1;  // may be < wrow0 for an empty wave
     const int wq_lo = L - qlen + (wrow0 < row_hi ? wrow0 / g : 0);
     const int wq_hi = L - qlen + (wrow1 >= wrow0 ? wrow1 / g : 0);
