@@ -204,6 +204,50 @@ def load_traffic(name, launches_bytes):
     return d.get("hbm_bytes_per_launch")
 
 
+def ceilings(device):
+    """What the vendor stack reaches on this GPU for the two bounds: a large bf16 GEMM through
+    torch.matmul (hipBLASLt) and a device-to-device copy (bytes read + written).  Context for the
+    roofline fractions, which are quoted against the published peaks."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = {}
+    n = 8192
+    a = torch.randn((n, n), device=device).to(torch.bfloat16)
+    b = torch.randn((n, n), device=device).to(torch.bfloat16)
+    c = torch.empty((n, n), device=device, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    out["bf16_gemm_8192_tflops"] = round(2 * n ** 3 / s / 1e12, 1)
+    out["bf16_gemm_frac_of_peak"] = round(2 * n ** 3 / s / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del a, b, c
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    out["copy_2gib_gbs"] = round(2 * src.numel() / s / 1e9, 1)
+    out["copy_frac_of_peak"] = round(2 * src.numel() / s / 1e9 / HBM_PEAK_GBS, 4)
+    out["note"] = "GEMM: 2 n^3 flop per torch.matmul, n = 8192; copy: 2 GiB read + 2 GiB written per copy"
+    del src, dst
+    return out
+
+
 def mixed_leg(device, reps):
     """GPU time of one mixed batch (64 decode requests and 4 prefill chunks): the mixed launch
     (both tile classes in one persistent kernel, then the state merge) against the decode
@@ -276,7 +320,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling aid: run just this workload (decode|prefill|append|strides|composable|rope|mixed)")
+                    help="profiling aid: run just this workload (decode|prefill|append|strides|composable|rope|mixed|ceilings)")
     ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
                     help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
     ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
@@ -507,44 +551,64 @@ def main():
     if not args.no_secondary and args.only in ("", "composable"):
         log("composable: shared 16384-token dense prefix + 64 paged suffixes")
         c = W.shared_prefix()
-        from block_sparse_kv_plan_amd.attention import merge_pair
-        pre = Runner(c.prefix, args.prefill_tile, copies=1, device=device)
-        suf = Runner(c.suffix, bsk.TILE_DECODE, copies=1, device=device)
-        fin_o = torch.empty_like(suf.out)
-        fin_l = torch.empty_like(suf.lse)
+        from block_sparse_kv_plan_amd.attention import run_composable
         stream = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
         n = max(10, args.steps // 2)
-
-        def one(i):
-            pre.step(i, stream)
-            suf.step(i, stream)
-            merge_pair(pre.out, pre.lse, suf.out, suf.lse, fin_o, fin_l, stream)
-
-        for i in range(3):
-            one(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        t0 = time.perf_counter()
-        for i in range(n):
-            one(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / n
-        gpu = e0.elapsed_time(e1) * 1e-3 / n
+        cus = torch.cuda.get_device_properties(device).multi_processor_count
         pb = 16384 * 8 * 128 * 2 * 2
         sb = decode_bytes(c.suffix)
-        secondary["shared_prefix_composable"] = {
-            "workload": "shared_prefix_composable_bf16: 16384-token dense prefix + 64 paged suffixes uniform "
-                        "[128,1024], 32q/8kv, d128",
-            "gpu_us_per_step": round(gpu * 1e6, 1), "wall_us_per_step": round(wall * 1e6, 1),
-            "effective_gbs": round((pb + sb) / gpu / 1e9, 1), "algorithmic_bytes": pb + sb}
-        del pre, suf
-        torch.cuda.empty_cache()
+        leg = {"workload": "shared_prefix_composable_bf16: 16384-token dense prefix + 64 paged suffixes uniform "
+                           "[128,1024], 32q/8kv, d128",
+               "algorithmic_bytes": pb + sb}
+        # sequential: each part on the whole GPU, one after the other; concurrent: each part planned
+        # for half the GPU, the suffix on a side stream beside the prefix
+        for label, workers, side_stream in (("sequential", (None, None), None), ("concurrent", (cus, cus), side)):
+            kw_p = {"num_workers": workers[0]} if workers[0] else {}
+            kw_s = {"num_workers": workers[1]} if workers[1] else {}
+            pre = Runner(c.prefix, args.prefill_tile, copies=1, device=device, **kw_p)
+            suf = Runner(c.suffix, bsk.TILE_DECODE, copies=1, device=device, **kw_s)
+            fin_o = torch.empty_like(suf.out)
+            fin_l = torch.empty_like(suf.lse)
+
+            a, b = pre.attn[0], suf.attn[0]
+            t0 = time.perf_counter()
+            a.plan(c.prefix.qo_indptr, c.prefix.kv_len, pre.kv_indptr, stream=stream)
+            b.plan(c.suffix.qo_indptr, c.suffix.kv_len, suf.kv_indptr, stream=stream)
+            plan_us = (time.perf_counter() - t0) * 1e6
+
+            def one():
+                run_composable(a, pre.tensors[0], (pre.out, pre.lse), b, suf.tensors[0], (suf.out, suf.lse),
+                               fin_o, fin_l, stream=stream, side_stream=side_stream)
+
+            for _ in range(3):
+                one()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                one()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gpu = e0.elapsed_time(e1) * 1e-3 / n
+            leg[label] = {"gpu_us_per_step": round(gpu * 1e6, 1), "effective_gbs": round((pb + sb) / gpu / 1e9, 1),
+                          "host_plans_us": round(plan_us, 1), "prefix_workers": a.info.num_workers,
+                          "suffix_workers": b.info.num_workers}
+            del pre, suf
+            torch.cuda.empty_cache()
+        leg["note"] = ("GPU time of prefix run + suffix run (each with its merge) + the LSE merge of the two "
+                       "states, plans built once (the prefix plan depends only on lengths); host_plans_us is the "
+                       "two host plans + uploads")
+        secondary["shared_prefix_composable"] = leg
 
     if not args.no_secondary and args.only in ("", "mixed"):
         log("mixed: 64 decode requests + 4 prefill chunks, one mixed launch vs decode + prefill launches")
         secondary["mixed_batch"] = mixed_leg(device, reps=max(10, args.steps // 2))
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and args.only in ("", "ceilings"):
+        log("ceilings: bf16 GEMM through torch (vendor BLAS) and a plain device copy, as practical context")
+        secondary["practical_ceilings"] = ceilings(device)
         torch.cuda.empty_cache()
 
     if result:

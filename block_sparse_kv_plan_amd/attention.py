@@ -146,6 +146,34 @@ def merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
                      stream or torch.cuda.current_stream(o_a.device))
 
 
+def run_composable(prefix: BatchAttention, prefix_tensors: Tensors, prefix_state, suffix: BatchAttention,
+                   suffix_tensors: Tensors, suffix_state, out, lse, stream=None, side_stream=None):
+    """Composable format (FlashInfer paper summary, "Research methodology" 1): attention over a
+    dense shared prefix and over each request's paged suffix, each with its own kernel and block
+    size, then the two states merged by LSE into (out, lse).
+
+    Both parts must already be planned; each run writes its own state into the (O f32, LSE) pair
+    its tensors name, passed again as prefix_state / suffix_state for the merge.  With a side stream the suffix runs there while the prefix runs on
+    `stream` -- the prefix is MFMA-bound and the suffix HBM-bound, so the two overlap when each
+    plan was made for part of the GPU (num_workers below bsk_device_workers) -- and `stream` waits
+    for the side stream before the merge.  Without one, the three steps run in order on `stream`.
+    Both orders give identical results (the plans fix every partial state and merge)."""
+    stream = stream or torch.cuda.current_stream(out.device)
+    if side_stream is not None:
+        start = torch.cuda.Event()
+        start.record(stream)
+        side_stream.wait_event(start)
+        suffix.run(suffix_tensors, stream=side_stream)
+        prefix.run(prefix_tensors, stream=stream)
+        done = torch.cuda.Event()
+        done.record(side_stream)
+        stream.wait_event(done)
+    else:
+        prefix.run(prefix_tensors, stream=stream)
+        suffix.run(suffix_tensors, stream=stream)
+    merge_pair(prefix_state[0], prefix_state[1], suffix_state[0], suffix_state[1], out, lse, stream)
+
+
 def pool_strides(pool, layout="HND"):
     """(page, head, token) element strides of a K or V pool tensor."""
     if layout == "HND":

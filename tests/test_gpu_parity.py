@@ -280,6 +280,34 @@ def test_shared_prefix_composable_full(prefix_tile):
     compare(suf, O, L, ref=ref)
 
 
+def test_composable_concurrent_matches_sequential():
+    """run_composable with the suffix on a side stream (each part planned for half the GPU) gives
+    the same bits as the sequential order, and the oracle's composable result."""
+    dev = require_gpu()
+    c = W.shared_prefix()
+    pre, suf = c.prefix, c.suffix
+    say("composable: concurrent vs sequential")
+    from block_sparse_kv_plan_amd.attention import run_composable
+    parts = []
+    for bb, tq in ((pre, bsk.TILE_PREFILL), (suf, bsk.TILE_DECODE)):
+        _, _, attn, (t, o, l, d, _) = run(bb, tile_q=tq, num_workers=256)
+        parts.append((attn, t, (o, l)))
+    outs = []
+    for side in (None, torch.cuda.Stream()):
+        fo = torch.full((64, 32, 128), float("nan"), dtype=torch.float32, device=dev)
+        fl = torch.full((64, 32), float("nan"), dtype=torch.float32, device=dev)
+        for i in range(3):  # repeated runs reuse the same plans
+            run_composable(parts[0][0], parts[0][1], parts[0][2], parts[1][0], parts[1][1], parts[1][2], fo, fl,
+                           side_stream=side)
+        torch.cuda.synchronize()
+        outs.append((fo.double().cpu().numpy(), fl.double().cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    from oracle.attention import DenseKV
+    ref = oracle.composable(suf.q, DenseKV(pre.dense_k, pre.dense_v, pre.kv_indptr), 16384,
+                            oracle_kv(suf, physical=True), suf.kv_len, suf.num_kv_heads, suf.sm_scale)
+    compare(suf, outs[1][0], outs[1][1], ref=ref)
+
+
 # ------------------------------------------------------------------ fused RoPE + window + sinks
 
 def test_streaming_rope_full():
