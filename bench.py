@@ -7,7 +7,7 @@ Headline: paged GQA decode of a Llama-3-8B-shaped layer (batch 64, 32 q / 8
 kv heads, head_dim 128, bf16, page 16, kv lengths lognormal in [512, 8192]).
 One step = host plan + plan upload + decode kernel + state merge, i.e. the
 whole hot path for one batch; two workspaces alternate so the host plan of
-step i+1 overlaps the GPU work of step i.  The KV cache is rotated over
+step i+1 and its upload (on a copy stream) overlap the GPU work of step i.  The KV cache is rotated over
 four device copies so no step reads what the previous one left in the
 256 MB Infinity Cache.  ``value`` is algorithmic bytes (visible K/V + q +
 out + lse + page ids) per wall-clock step, in TB/s.
@@ -127,10 +127,10 @@ class Runner:
         a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, copy_stream=copy_stream)
         t = self.tensors[i % len(self.tensors)]
         if copy_stream is not None:
-            stream.wait_event(a._uploaded)
+            stream.wait_event(a._uploaded)  # before the kernel's start event, so that it times the kernel only
         if ev is not None:
             ev[0].record(stream)
-        a.run(t, stream=stream, merge=False)
+        a.run(t, stream=stream, merge=False, wait_upload=copy_stream is None)
         if ev is not None:
             ev[1].record(stream)
         if not a.problem.fused_merge:
@@ -141,24 +141,28 @@ class Runner:
 
 def timed(runner, steps, warmup):
     """Wall time per step over `steps` back-to-back steps, and the attention kernel's and the
-    merge's mean durations from events on their launch stream."""
+    merge's mean durations from events on their launch stream.  Plans are uploaded on a copy
+    stream (off the kernels' queue); the kernel / merge events are recorded on every fourth
+    timed step (every step when there are fewer than 20), since each event is a packet on the
+    kernels' queue and costs a few microseconds of its own."""
     import torch
     stream = torch.cuda.current_stream()
-    copy_stream = None  # a separate upload queue measured slower (cross-queue waits) than in-stream copies
+    copy_stream = torch.cuda.Stream()
+    every = 4 if steps >= 20 else 1
     for i in range(warmup):
         runner.step(i, stream, copy_stream=copy_stream)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] if i % every == 0 else None for i in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         runner.step(warmup + i, stream, evs[i], copy_stream=copy_stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    kern = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
-    merge = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
+    kern = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs if e is not None]
+    merge = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs if e is not None]
     kern.sort()
     return {"wall_s": wall, "kernel_s_mean": sum(kern) / len(kern), "kernel_s_median": kern[len(kern) // 2],
-            "kernel_s_min": kern[0], "merge_s_mean": sum(merge) / len(merge)}
+            "kernel_s_min": kern[0], "merge_s_mean": sum(merge) / len(merge), "event_samples": len(kern)}
 
 
 def cpu_baseline(batch, budget_s=15.0):
@@ -390,6 +394,7 @@ def main():
                          "traffic": traffic, "kernel": "decode_kernel<bf16,128,paged>",
                          "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2),
                          "kernel_us_median": round(m["kernel_s_median"] * 1e6, 2),
+                         "event_samples": m["event_samples"],
                          "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
                          "algorithmic_bytes_per_launch": nbytes},
         }

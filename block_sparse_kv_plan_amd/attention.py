@@ -123,9 +123,12 @@ class BatchAttention:
         self._upload_stream = up
         return self.info
 
-    def run(self, tensors: Tensors, stream=None, merge: bool = True):
+    def run(self, tensors: Tensors, stream=None, merge: bool = True, wait_upload: bool = True):
+        """Attention (and, unless merge is False, the merge) for the last plan.  A plan uploaded on
+        another stream is waited for on `stream` first; wait_upload=False leaves that wait to the
+        caller (who must have made `stream` wait for the upload already)."""
         stream = stream or torch.cuda.current_stream(self.device)
-        if self._upload_stream is not None and self._upload_stream != stream:
+        if wait_upload and self._upload_stream is not None and self._upload_stream != stream:
             stream.wait_event(self._uploaded)
         if self.problem.tile_q == TILE_DECODE:
             run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)

@@ -333,6 +333,45 @@ def test_rope_head_dim_64():
     compare(b, O, L)
 
 
+# ------------------------------------------------------------------ plan upload on a copy stream
+
+def test_copy_stream_uploads_alternating_plans():
+    """Two plan workspaces used alternately, a different batch (lengths, hence plan) every step,
+    each plan uploaded on a side stream while the main stream still runs earlier steps: every
+    step's output equals the same step run with in-stream uploads, bit for bit, and the oracle."""
+    dev = require_gpu()
+    Hq, Hk, d = 32, 8, 128
+    rng = np.random.default_rng(83)
+    batches = [small(83 + i, rng.integers(1, 3000, size=int(rng.integers(3, 12))), Hq=Hq, Hk=Hk, d=d, causal=True)
+               for i in range(6)]
+    say("copy-stream plan uploads over 6 steps")
+    attn = [BatchAttention.create(device=dev, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=d, dtype=bsk.DTYPE_BF16,
+                                  causal=True, max_batch=16) for _ in range(2)]
+    dus = [upload(bb) for bb in batches]
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def outputs():
+        return [(torch.full((int(bb.qo_indptr[-1]), Hq, d), float("nan"), dtype=torch.float32, device=dev),
+                 torch.full((int(bb.qo_indptr[-1]), Hq), float("nan"), dtype=torch.float32, device=dev))
+                for bb in batches]
+
+    results = []
+    for copy_stream in (None, side):
+        outs = outputs()
+        torch.cuda.synchronize()
+        for i, (bb, du) in enumerate(zip(batches, dus)):
+            a = attn[i % 2]
+            t = tensors_for(a.problem, du["q"], du["k"], du["v"], outs[i][0], outs[i][1], page_indices=du["pages"])
+            a.plan(bb.qo_indptr, bb.kv_len, du["kv_indptr"], stream=main, copy_stream=copy_stream)
+            a.run(t, stream=main)
+        torch.cuda.synchronize()
+        results.append([(o.double().cpu().numpy(), l.double().cpu().numpy()) for o, l in outs])
+    for i, bb in enumerate(batches):
+        assert np.array_equal(results[0][i][0], results[1][i][0]) and np.array_equal(results[0][i][1], results[1][i][1])
+        compare(bb, results[1][i][0], results[1][i][1])
+
+
 # ------------------------------------------------------------------ graph capture
 
 def test_graph_capture_replan_replay():
