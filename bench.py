@@ -103,8 +103,11 @@ class Runner:
         self.attn = [make_attention(batch, tile_q, out_dtype, device, **plan_kw) for _ in range(2)]
         T = int(batch.qo_indptr[-1])
         o_dt = torch.bfloat16 if out_dtype == bsk.DTYPE_BF16 else torch.float32
-        self.out = torch.zeros((T, batch.num_qo_heads, batch.head_dim), dtype=o_dt, device=device)
-        self.lse = torch.zeros((T, batch.num_qo_heads), dtype=torch.float32, device=device)
+        # one output pair per KV copy, so that consecutive steps never write the same buffers
+        self.outs = [(torch.zeros((T, batch.num_qo_heads, batch.head_dim), dtype=o_dt, device=device),
+                      torch.zeros((T, batch.num_qo_heads), dtype=torch.float32, device=device))
+                     for _ in range(copies)]
+        self.out, self.lse = self.outs[0]
         self.rope = None
         if batch.rope != "none":
             n_pos = rope_positions_needed(batch)
@@ -116,13 +119,12 @@ class Runner:
         self.dev.append(first)
         for _ in range(copies - 1):
             self.dev.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in first.items()})
-        self.tensors = [tensors_for(self.attn[0].problem, d["q"], d["k"], d["v"], self.out, self.lse,
-                                    page_indices=d["pages"], rope=self.rope) for d in self.dev]
+        self.tensors = [tensors_for(self.attn[0].problem, d["q"], d["k"], d["v"], o, l,
+                                    page_indices=d["pages"], rope=self.rope) for d, (o, l) in zip(self.dev, self.outs)]
 
     def step(self, i, stream, ev=None, copy_stream=None):
         """One pass of the hot path: host plan + upload (on the copy stream when given),
         the attention kernel, then the split-KV state merge."""
-        import block_sparse_kv_plan_amd as bsk
         a = self.attn[i % 2]
         a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, copy_stream=copy_stream)
         t = self.tensors[i % len(self.tensors)]
@@ -133,8 +135,7 @@ class Runner:
         a.run(t, stream=stream, merge=False, wait_upload=copy_stream is None)
         if ev is not None:
             ev[1].record(stream)
-        if not a.problem.fused_merge:
-            bsk.merge_states(a.problem, a.info, t, a.int_ws, a.float_ws, stream)
+        a.merge(t, stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -142,7 +143,8 @@ class Runner:
 def timed(runner, steps, warmup):
     """Wall time per step over `steps` back-to-back steps, and the attention kernel's and the
     merge's mean durations from events on their launch stream.  Plans are uploaded on a copy
-    stream (off the kernels' queue); the kernel / merge events are recorded on every fourth
+    stream (off the kernels' queue; a third stream for the merges measured slower); the
+    kernel / merge events are recorded on every fourth
     timed step (every step when there are fewer than 20), since each event is a packet on the
     kernels' queue and costs a few microseconds of its own."""
     import torch
@@ -153,6 +155,9 @@ def timed(runner, steps, warmup):
         runner.step(i, stream, copy_stream=copy_stream)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] if i % every == 0 else None for i in range(steps)]
+    for e in (x for trio in evs if trio is not None for x in trio):
+        e.record(stream)  # torch creates the HIP event at its first record: do that outside the timed region
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         runner.step(warmup + i, stream, evs[i], copy_stream=copy_stream)

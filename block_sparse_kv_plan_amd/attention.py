@@ -85,9 +85,10 @@ def tensors_for(problem: Problem, q, k, v, out, lse, page_indices=None, layout: 
 class BatchAttention:
     """Owns the workspaces of one problem; plan() per step, run() per layer.
 
-    The plan upload can go on its own copy stream: it then waits (on the GPU)
-    for the previous run that read this workspace, and run() waits for the
-    upload, so a host plan plus its copy overlap the GPU work already queued."""
+    The plan upload can go on its own copy stream, and the merge can run on a stream of its own
+    (merge()): an upload waits (on the GPU) for the last run and the last merge that read this
+    workspace on other streams, and run() waits for the upload, so a host plan, its copy and the
+    previous step's merge overlap the GPU work already queued."""
 
     def __init__(self, problem: Problem, device="cuda"):
         self.problem = problem
@@ -99,9 +100,11 @@ class BatchAttention:
         self.info: Optional[PlanInfo] = None
         self._uploaded = torch.cuda.Event()   # the plan copy out of host_ws has completed
         self._consumed = torch.cuda.Event()   # the last run reading int_ws has completed
+        self._merged = torch.cuda.Event()     # the last merge reading int_ws / float_ws has completed
+        self._consumed_stream = None
+        self._merged_stream = None
         self._upload_pending = False
         self._upload_stream = None
-        self._ran = False
 
     @classmethod
     def create(cls, *, device="cuda", num_workers=None, **kw):
@@ -114,8 +117,16 @@ class BatchAttention:
             self._uploaded.synchronize()  # host_ws is still being read by the previous copy
         stream = stream or torch.cuda.current_stream(self.device)
         up = copy_stream if copy_stream is not None else stream
-        if copy_stream is not None and self._ran:
-            up.wait_event(self._consumed)  # do not overwrite int_ws under a running kernel
+        # do not overwrite int_ws under a kernel that still reads it on another stream: wait for the
+        # last run and the last merge (one wait when both went to the same stream, the merge last)
+        waits = []
+        if self._merged_stream is not None:
+            waits.append((self._merged, self._merged_stream))
+        if self._consumed_stream is not None and self._consumed_stream != self._merged_stream:
+            waits.append((self._consumed, self._consumed_stream))
+        for ev, st in waits:
+            if st != up:
+                up.wait_event(ev)
         self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
                          self.host_ws, self.int_ws, up)
         self._uploaded.record(up)
@@ -134,10 +145,21 @@ class BatchAttention:
             run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         else:
             run_prefill(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
-        if merge and not self.problem.fused_merge:
-            merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         self._consumed.record(stream)
-        self._ran = True
+        self._consumed_stream = stream
+        self._merged_stream = None  # the last merge event belongs to an earlier run
+        if merge:
+            self.merge(tensors, stream)
+
+    def merge(self, tensors: Tensors, stream=None):
+        """The split-KV merge of the last run (nothing when the run merged in-kernel).  On another
+        stream than the run's, the caller makes that stream wait for the run first."""
+        if self.problem.fused_merge:
+            return
+        stream = stream or torch.cuda.current_stream(self.device)
+        merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        self._merged.record(stream)
+        self._merged_stream = stream
 
 
 def merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):

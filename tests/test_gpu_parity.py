@@ -337,8 +337,9 @@ def test_rope_head_dim_64():
 
 def test_copy_stream_uploads_alternating_plans():
     """Two plan workspaces used alternately, a different batch (lengths, hence plan) every step,
-    each plan uploaded on a side stream while the main stream still runs earlier steps: every
-    step's output equals the same step run with in-stream uploads, bit for bit, and the oracle."""
+    each plan uploaded on a side stream while the main stream still runs earlier steps, and the
+    merges on a third stream: every step's output equals the same step run in one stream, bit for
+    bit, and the oracle."""
     dev = require_gpu()
     Hq, Hk, d = 32, 8, 128
     rng = np.random.default_rng(83)
@@ -356,20 +357,30 @@ def test_copy_stream_uploads_alternating_plans():
                  torch.full((int(bb.qo_indptr[-1]), Hq), float("nan"), dtype=torch.float32, device=dev))
                 for bb in batches]
 
+    merge_side = torch.cuda.Stream()
     results = []
-    for copy_stream in (None, side):
+    # in-stream; uploads on a copy stream; uploads and merges each on a stream of their own
+    for copy_stream, merge_stream in ((None, None), (side, None), (side, merge_side)):
         outs = outputs()
         torch.cuda.synchronize()
         for i, (bb, du) in enumerate(zip(batches, dus)):
             a = attn[i % 2]
             t = tensors_for(a.problem, du["q"], du["k"], du["v"], outs[i][0], outs[i][1], page_indices=du["pages"])
             a.plan(bb.qo_indptr, bb.kv_len, du["kv_indptr"], stream=main, copy_stream=copy_stream)
-            a.run(t, stream=main)
+            if merge_stream is None:
+                a.run(t, stream=main)
+            else:
+                a.run(t, stream=main, merge=False)
+                done = torch.cuda.Event()
+                done.record(main)
+                merge_stream.wait_event(done)
+                a.merge(t, merge_stream)
         torch.cuda.synchronize()
         results.append([(o.double().cpu().numpy(), l.double().cpu().numpy()) for o, l in outs])
     for i, bb in enumerate(batches):
-        assert np.array_equal(results[0][i][0], results[1][i][0]) and np.array_equal(results[0][i][1], results[1][i][1])
-        compare(bb, results[1][i][0], results[1][i][1])
+        for r in results[1:]:
+            assert np.array_equal(results[0][i][0], r[i][0]) and np.array_equal(results[0][i][1], r[i][1])
+        compare(bb, results[2][i][0], results[2][i][1])
 
 
 # ------------------------------------------------------------------ graph capture
