@@ -177,10 +177,13 @@ def cpu_baseline(batch, budget_s=15.0):
 
     import numpy as np
 
+    from threadpoolctl import threadpool_limits
+
     import oracle
     from tests.helpers import oracle_kv
     kv = oracle_kv(batch)  # host view of the cache, built once outside the timed calls
     done, t_used, bytes_done = 0, 0.0, 0
+    limits = threadpool_limits(limits=1)  # the oracle's one BLAS product runs single-threaded too
     for r in range(batch.batch_size):
         sub = copy.copy(batch)
         t0 = time.perf_counter()
@@ -195,9 +198,10 @@ def cpu_baseline(batch, budget_s=15.0):
         done += 1
         if t_used > budget_s:
             break
+    limits.restore_original_limits()
     return {"value": bytes_done / t_used / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {batch.batch_size} requests of the same batch (fp64 numpy, single-threaded "
-                      f"einsum path), {t_used:.1f} s"}
+            "sample": f"{done} of {batch.batch_size} requests of the same batch (fp64 numpy; einsum for the "
+                      f"logits, BLAS held to one thread for the P V product), {t_used:.1f} s"}
 
 
 def load_traffic(name, launches_bytes):
