@@ -145,12 +145,12 @@ def timed(runner, steps, warmup):
     merge's mean durations from events on their launch stream.  Plans are uploaded on a copy
     stream (off the kernels' queue; a third stream for the merges measured slower); the
     kernel / merge events are recorded on every fourth
-    timed step (every step when there are fewer than 20), since each event is a packet on the
+    timed step (every step when there are fewer than 80), since each event is a packet on the
     kernels' queue and costs a few microseconds of its own."""
     import torch
     stream = torch.cuda.current_stream()
     copy_stream = torch.cuda.Stream()
-    every = 4 if steps >= 20 else 1
+    every = 4 if steps >= 80 else 1
     for i in range(warmup):
         runner.step(i, stream, copy_stream=copy_stream)
     torch.cuda.synchronize()
@@ -166,8 +166,27 @@ def timed(runner, steps, warmup):
     kern = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs if e is not None]
     merge = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs if e is not None]
     kern.sort()
-    return {"wall_s": wall, "kernel_s_mean": sum(kern) / len(kern), "kernel_s_median": kern[len(kern) // 2],
-            "kernel_s_min": kern[0], "merge_s_mean": sum(merge) / len(merge), "event_samples": len(kern)}
+    pct = lambda q: kern[min(len(kern) - 1, int(q * len(kern)))]
+    return {"wall_s": wall, "kernel_s_mean": sum(kern) / len(kern), "kernel_s_median": pct(0.5),
+            "kernel_s_p10": pct(0.1), "kernel_s_p90": pct(0.9), "kernel_s_min": kern[0],
+            "merge_s_mean": sum(merge) / len(merge), "event_samples": len(kern)}
+
+
+def plan_host_us(runner, calls=50):
+    """Mean host time of the C++ plan for the runner's batch (no upload)."""
+    import numpy as np
+
+    import block_sparse_kv_plan_amd as bsk
+    b, a = runner.batch, runner.attn[0]
+    qo = np.ascontiguousarray(b.qo_indptr, dtype=np.int32)
+    kl = np.ascontiguousarray(b.kv_len, dtype=np.int32)
+    ki = np.ascontiguousarray(runner.kv_indptr, dtype=np.int32)
+    host = np.zeros(a.host_ws.numel(), dtype=np.uint8)  # a private buffer: no upload is in flight from it
+    bsk.plan(a.problem, qo, kl, ki, host)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        bsk.plan(a.problem, qo, kl, ki, host)
+    return round((time.perf_counter() - t0) / calls * 1e6, 1)
 
 
 def cpu_baseline(batch, budget_s=15.0):
@@ -199,9 +218,16 @@ def cpu_baseline(batch, budget_s=15.0):
         if t_used > budget_s:
             break
     limits.restore_original_limits()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": bytes_done / t_used / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {batch.batch_size} requests of the same batch (fp64 numpy; einsum for the "
-                      f"logits, BLAS held to one thread for the P V product), {t_used:.1f} s"}
+                      f"logits, BLAS held to one thread for the P V product), {t_used:.1f} s",
+            "cpu": model, "cores_available": len(os.sched_getaffinity(0)), "blas_threads": 1}
 
 
 def load_traffic(name, launches_bytes):
@@ -328,8 +354,8 @@ def mixed_leg(device, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
@@ -377,6 +403,7 @@ def main():
         m = timed(runner, args.steps, args.warmup)
         info = runner.attn[0].info
         achieved = nbytes / m["kernel_s_mean"] / 1e9
+        plan_us = plan_host_us(runner)
         traffic = load_traffic("decode_llama3", nbytes)
         result = {
             "metric": "paged decode HBM TB/s (% of 8 TB/s peak); ragged prefill TFLOPS (% MFMA peak)",
@@ -397,12 +424,15 @@ def main():
                        "out_dtype": "f32", "num_workers": info.num_workers, "items": info.num_items,
                        "chunk": info.chunk, "merges": info.num_merge,
                        "plan_imbalance": round(info.max_load / max(1.0, info.total_cost / info.num_workers), 3),
+                       "plan_host_us": plan_us,
                        "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "kernel": "decode_kernel<bf16,128,paged>",
                          "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2),
                          "kernel_us_median": round(m["kernel_s_median"] * 1e6, 2),
+                         "kernel_us_p10": round(m["kernel_s_p10"] * 1e6, 2),
+                         "kernel_us_p90": round(m["kernel_s_p90"] * 1e6, 2),
                          "event_samples": m["event_samples"],
                          "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
                          "algorithmic_bytes_per_launch": nbytes},
