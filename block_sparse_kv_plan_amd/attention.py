@@ -20,8 +20,8 @@ TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
 # Plan defaults per query-tile class: (tile_kv, split_factor, min_chunk, max_items_per_worker)
 DEFAULTS = {
     TILE_DECODE: dict(tile_kv=16, split_factor=2, min_chunk=512, max_items_per_worker=64),
-    TILE_PREFILL: dict(tile_kv=64, split_factor=1, min_chunk=256, max_items_per_worker=64),
-    TILE_PREFILL_256: dict(tile_kv=64, split_factor=1, min_chunk=256, max_items_per_worker=64),
+    TILE_PREFILL: dict(tile_kv=64, split_factor=1, min_chunk=1024, max_items_per_worker=64),
+    TILE_PREFILL_256: dict(tile_kv=64, split_factor=1, min_chunk=1024, max_items_per_worker=64),
 }
 
 
