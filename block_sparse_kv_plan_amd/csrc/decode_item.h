@@ -32,9 +32,10 @@
 // f32 inputs use the 16x16x4 f32 MFMA (one k element per lane), which
 // reads V straight from memory.
 //
-// Fused RoPE (bf16): q and every key are rotated in fp32 with a cos/sin
-// table (the cache holds K unrotated), then split into bf16 hi + lo parts so
-// the MFMA logits keep ~16 significant bits: S = Kh.Qh + Kh.Ql + Kl.Qh.
+// Fused RoPE (bf16 cache): q and every key are rotated in fp32 with a cos/sin
+// table (the cache holds K unrotated) and rounded to fp16, whose 11-bit
+// significand keeps the logits' rounding error 8x below bf16's, so the
+// logits come from one fp16 MFMA per k-step.
 
 #pragma once
 
@@ -77,18 +78,19 @@ __device__ __forceinline__ void unpack_bf16x8(const bf16x8& v, float* f) {
   }
 }
 
-// f (8 floats) -> hi = bf16(f), lo = bf16(f - hi)
-__device__ __forceinline__ void split_bf16x8(const float* f, bf16x8& hi, bf16x8& lo) {
-  u32x4 h, l;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// 8 floats -> fp16x8, rounded to nearest even (four packed conversions)
+__device__ __forceinline__ f16x8 to_f16x8(const float* f) {
+  f16x8 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t h0 = f32_to_bf16_bits(f[2 * e]);
-    const uint32_t h1 = f32_to_bf16_bits(f[2 * e + 1]);
-    h[e] = h0 | (h1 << 16);
-    l[e] = pack_bf16x2(f[2 * e] - __uint_as_float(h0 << 16), f[2 * e + 1] - __uint_as_float(h1 << 16));
+    const f16x2_t h = __builtin_convertvector((f32x2{f[2 * e], f[2 * e + 1]}), f16x2_t);
+    r[2 * e] = h[0];
+    r[2 * e + 1] = h[1];
   }
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = __builtin_bit_cast(bf16x8, l);
+  return r;
 }
 
 // Element e of four 8-element pieces (a, b, c, d), as an MFMA k-quad.
@@ -171,7 +173,8 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
       n_s = a.window > 0 ? min(a.sink, lo_w) : 0;
     }
 
-    bf16x8 qh[BF ? NKS : 1], ql[BF && ROPE != ROPE_NONE ? NKS : 1];
+    bf16x8 qh[BF ? NKS : 1];
+    f16x8 qr[BF && ROPE != ROPE_NONE ? NKS : 1];  // rotated q in fp16 (fused RoPE)
     float qf[BF ? 1 : NKS];
     if constexpr (BF) {
 #pragma unroll
@@ -187,12 +190,12 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
           unpack_bf16x8(qh[s], lo);
           unpack_bf16x8(qh[s + HALF_KS], hi);
           rope8(lo, hi, a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2);
-          split_bf16x8(lo, qh[s], ql[s]);
-          split_bf16x8(hi, qh[s + HALF_KS], ql[s + HALF_KS]);
+          qr[s] = to_f16x8(lo);
+          qr[s + HALF_KS] = to_f16x8(hi);
         }
         if (!row_ok) {
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) qh[s] = ql[s] = bf16x8{};
+          for (int s = 0; s < NKS; ++s) qr[s] = f16x8{};
         }
       }
     } else {
@@ -284,22 +287,18 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
           const int tk = min(max(tb + kkey, kmin), kmax);
           int pk = ROPE == ROPE_STREAMING ? (tk < n_s ? tk : n_s + (tk - lo_w)) : tk;
           pk = min(max(pk, 0), a.rope_n_pos - 1);
-          bf16x8 kl[NKS];
+          f16x8 kr[NKS];
 #pragma unroll
           for (int s = 0; s < HALF_KS; ++s) {
             float lo[8], hi[8];
             unpack_bf16x8(kf[s], lo);
             unpack_bf16x8(kf[s + HALF_KS], hi);
             rope8(lo, hi, a.rope + (int64_t(pk) * (D / 2) + 8 * (4 * s + j)) * 2);
-            split_bf16x8(lo, kf[s], kl[s]);
-            split_bf16x8(hi, kf[s + HALF_KS], kl[s + HALF_KS]);
+            kr[s] = to_f16x8(lo);
+            kr[s + HALF_KS] = to_f16x8(hi);
           }
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) {
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], ql[s], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[s], qh[s], st, 0, 0, 0);
-          }
+          for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[s], qr[s], st, 0, 0, 0);
         }
         // st[i]: logit of key tb + 4i + j for query row n
         float sv[4], p[4];

@@ -116,6 +116,6 @@ def test_unfused_rope_decode_matches_oracle(mode):
     # This baseline stores the rotated q and k in bf16 (unit roundoff u = 2^-8); a logit
     # scale * <q, k> then moves by up to about scale * |q| |k| u / sqrt(d) ~ u for unit-variance
     # rows, and the LSE, a probability-weighted mean of those moves, by a fraction of it.  The
-    # fused kernel avoids the rounding (hi/lo split) and is held to 1e-3; the unfused reference
+    # fused kernel rounds to fp16 instead (2^-11) and is held to 1e-3; the unfused reference
     # point gets 2e-3 on the LSE, O keeps 1e-2.
     compare(b, out.double().cpu().numpy(), lse.double().cpu().numpy(), lse_tol=2e-3)
