@@ -58,6 +58,12 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((2 * (r & 3)) ^ (8 * ((r >> 2) & 1))) : (2 * ((r >> 1) & 3));
 }
 
+// A compile-time value passed to a generic lambda.
+template <typename T, T V>
+struct Const {
+  static constexpr T value = V;
+};
+
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
@@ -168,8 +174,8 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
     // the wave's query-position range (rows past row_hi excluded), for the mask-free test
     const int wrow0 = row_lo + WROWS * wave_u;  // wave-uniform: the tile tests below stay scalar
     const int wrow1 = min(row_hi, wrow0 + WROWS) - 1;  // may be < wrow0 for an empty wave
-    const int wq_lo = L - qlen + (wrow0 < row_hi ? wrow0 / g : 0);
-    const int wq_hi = L - qlen + (wrow1 >= wrow0 ? wrow1 / g : 0);
+    const int wq_lo = __builtin_amdgcn_readfirstlane(L - qlen + (wrow0 < row_hi ? wrow0 / g : 0));
+    const int wq_hi = __builtin_amdgcn_readfirstlane(L - qlen + (wrow1 >= wrow0 ? wrow1 / g : 0));
     const bool wave_has_rows = wrow0 < row_hi;
     const bool all_rows = wrow0 + WROWS <= row_hi;
 
@@ -186,16 +192,26 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
     // Transfer addressing.  When tiles start at multiples of 64 keys (always for dense KV; for
     // paged KV when the item does), a full tile's row t sits in page slot (kt >> shift) - p0 +
     // (t >> shift) at in-page token (kt & pmask) + (t & pmask): a page of <= 64 keys divides the
-    // tile, a larger page holds all of it.  The 32-bit per-row part (head, in-page or in-tile
-    // token, chunk) is below the page stride (paged) or 2^31 (dense, checked by the host).
+    // tile (the in-page part of kt is zero), a larger page holds all of it.  The 32-bit per-row
+    // part (head, in-page or in-tile token, chunk) is below the page stride (paged) or 2^31
+    // (dense, checked by the host).  kfix[p] / vfix[p] are the K / V addresses of transfer p's
+    // row in page 0 (paged) or at key 0 (dense); with shared strides the V address is the K
+    // address plus vdel[p].
     const bool fast_item = DENSE || (kv_lo & (kPreKeys - 1)) == 0;
-    uint32_t koff[NP], voff[NP];
+    const char* kfix[NP];
+    const char* vfix[NP];
+    int64_t vdel[NP];
+    int pslot[NP];  // page slot of transfer p's row, relative to the tile's first slot
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int tok = DENSE ? trow[p] : (trow[p] & pmask);
-      koff[p] = uint32_t(2 * (int64_t(h) * a.k_sh + int64_t(tok) * a.k_st) + 16 * ck[p]);
-      voff[p] = SAME ? koff[p] - 16 * ck[p] + 16 * cv[p]
-                     : uint32_t(2 * (int64_t(h) * a.v_sh + int64_t(tok) * a.v_st) + 16 * cv[p]);
+      const uint32_t koff = uint32_t(2 * (int64_t(h) * a.k_sh + int64_t(tok) * a.k_st) + 16 * ck[p]);
+      const uint32_t voff = SAME ? koff - 16 * ck[p] + 16 * cv[p]
+                                 : uint32_t(2 * (int64_t(h) * a.v_sh + int64_t(tok) * a.v_st) + 16 * cv[p]);
+      kfix[p] = reinterpret_cast<const char*>(Kp) + koff;
+      vfix[p] = reinterpret_cast<const char*>(Vp) + voff;
+      vdel[p] = vfix[p] - kfix[p];
+      pslot[p] = trow[p] >> a.page_shift;
     }
     const int p0 = kv_lo >> a.page_shift;
 
@@ -203,29 +219,46 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
       const uint32_t lk0 = lds_k + uint32_t(buf * TILE * 2), lv0 = lds_v + uint32_t(buf * TILE * 2);
       if (fast_item && kt + kPreKeys <= kv_hi) {
         if constexpr (DENSE) {
-          const char* kb = reinterpret_cast<const char*>(Kp) + 2 * (int64_t(kbase + kt) * a.k_st);
-          const char* vb = reinterpret_cast<const char*>(Vp) + 2 * (int64_t(kbase + kt) * a.v_st);
+          const int64_t tk = 2 * (int64_t(kbase + kt) * a.k_st);
+          const int64_t tv = 2 * (int64_t(kbase + kt) * a.v_st);
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
             const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
-            dma16(kb + koff[p], lk0 + lo);
-            dma16(vb + voff[p], lv0 + lo);
+            const char* ka = kfix[p] + tk;
+            dma16(ka, lk0 + lo);
+            dma16(SAME ? ka + vdel[p] : vfix[p] + tv, lv0 + lo);
           }
         } else {
+          // All page ids first: the transfers are ordered memory operations, so an LDS read
+          // placed after one of them would wait on its own.
           const int sb = (kt >> a.page_shift) - p0;
-          const char* kb = reinterpret_cast<const char*>(Kp) + 2 * (int64_t(kt & pmask) * a.k_st);
-          const char* vb = reinterpret_cast<const char*>(Vp) + 2 * (int64_t(kt & pmask) * a.v_st);
+          uint32_t page[NP];
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const uint32_t page = uint32_t(s_pages[sb + (trow[p] >> a.page_shift)]);
-            const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
-            const uint64_t pk = uint64_t(page) * k_page_bytes + koff[p];
-            dma16(kb + pk, lk0 + lo);
-            if constexpr (SAME)  // the V row sits at the same offset; only its 16-byte chunk differs
-              dma16(vb + (int64_t(pk) + 16 * (cv[p] - ck[p])), lv0 + lo);
-            else
-              dma16(vb + (uint64_t(page) * v_page_bytes + voff[p]), lv0 + lo);
-          }
+          for (int p = 0; p < NP; ++p) page[p] = uint32_t(s_pages[sb + pslot[p]]);
+          // pages of more than 64 keys: the tile starts inside the page
+          auto issue = [&](auto big_c) {
+            constexpr bool BIG = decltype(big_c)::value;
+            const int64_t tk = BIG ? 2 * (int64_t(kt & pmask) * a.k_st) : 0;
+            const int64_t tv = BIG ? 2 * (int64_t(kt & pmask) * a.v_st) : 0;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+              const char* ka = kfix[p] + uint64_t(page[p]) * k_page_bytes;
+              if constexpr (BIG) ka += tk;
+              dma16(ka, lk0 + lo);
+              if constexpr (SAME) {
+                dma16(ka + vdel[p], lv0 + lo);
+              } else {
+                const char* va = vfix[p] + uint64_t(page[p]) * v_page_bytes;
+                if constexpr (BIG) va += tv;
+                dma16(va, lv0 + lo);
+              }
+            }
+          };
+          if (a.page_shift > 6)
+            issue(Const<bool, true>{});
+          else
+            issue(Const<bool, false>{});
         }
       } else {
         // ragged tail or unaligned start: rows past the range repeat the last key (masked later)
@@ -243,139 +276,163 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
     };
 
     const int ntiles = (kv_hi - kv_lo + kPreKeys - 1) / kPreKeys;  // items are never empty
-    wait_vm();  // q fragments and page ids are in registers before the tile loop starts
-    if (ntiles > 0) load_tile(kv_lo, 0);
-    for (int tile = 0; tile < ntiles; ++tile) {
+    // A tile starting at key kt needs no mask for any row of this wave iff clean_lo <= kt <=
+    // clean_hi: the wave's rows are all in the item, the tile ends inside the key range and at
+    // or before the wave's first query position (causal), and every key of it is inside the
+    // window of the wave's last query position.
+    int clean_hi = all_rows ? kv_hi - kPreKeys : INT_MIN;
+    if (a.causal) clean_hi = min(clean_hi, wq_lo - (kPreKeys - 1));
+    const int clean_lo = a.window > 0 ? wq_hi - a.window + 1 : INT_MIN;
+    clean_hi = __builtin_amdgcn_readfirstlane(clean_hi);
+
+    // Per row block besides m_run and l_run: the exponent offset (-m_run, or 0 before any
+    // visible key) and the raw logit above which the reference has to move.
+    const float inv_scale_log2 = 1.f / a.scale_log2;
+    float neg_m[NB], thr[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      neg_m[nb] = 0.f;
+      thr[nb] = -INFINITY;
+    }
+
+    // One 64-key tile from LDS buffer BUF, a compile-time constant so that every LDS read
+    // address is a per-lane constant plus an immediate offset.
+    auto tile_step = [&](int tile, auto buf_c) {
+      constexpr int BUF = decltype(buf_c)::value;
       const int kt = kv_lo + tile * kPreKeys;
-      const int buf = tile & 1;
       wait_dma();        // this wave's transfers of the tile have landed
       __syncthreads();   // ... and every other wave's; the other buffer is free again
-      if (tile + 1 < ntiles) load_tile(kt + kPreKeys, buf ^ 1);  // in flight during this tile's math
-      const unsigned short* sk = s_k + buf * TILE;
-      const unsigned short* sv = s_v + buf * TILE;
+      if (tile + 1 < ntiles) load_tile(kt + kPreKeys, BUF ^ 1);  // in flight during this tile's math
+      if (!wave_has_rows) return;
+      const unsigned short* sk = s_k + BUF * TILE;
+      const unsigned short* sv = s_v + BUF * TILE;
 
-      if (wave_has_rows) {
-        // masks only where the tile crosses a boundary for some row of this wave
-        const int kend = kt + kPreKeys - 1;
-        bool clean = all_rows && kend < kv_hi;
-        if (a.causal) clean = clean && kend <= wq_lo;
-        if (a.window > 0) clean = clean && (wq_hi - kt) < a.window;
-        // Logits of a 32-key half: all its K fragments are read first (their LDS latencies
-        // overlap), then the MFMAs.
-        auto logits = [&](int ks, f32x4 (&st)[2][NB]) {
+      // masks only where the tile crosses a boundary for some row of this wave
+      const bool clean = kt >= clean_lo && kt <= clean_hi;
+      // Logits of a 32-key half: all its K fragments are read first (their LDS latencies
+      // overlap), then the MFMAs.
+      auto logits = [&](int ks, f32x4 (&st)[2][NB]) {
+#pragma unroll
+        for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) st[mh][nb] = f32x4{0, 0, 0, 0};
+        bf16x8 kf[2][NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+#pragma unroll
+          for (int mh = 0; mh < 2; ++mh)
+            kf[mh][s] = *reinterpret_cast<const bf16x8*>(sk + 16 * (2 * ks + mh) * D + k_rd + 8 * ((4 * s + j) ^ k_sw));
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
 #pragma unroll
           for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) st[mh][nb] = f32x4{0, 0, 0, 0};
-          bf16x8 kf[2][NKS];
+            for (int nb = 0; nb < NB; ++nb)
+              st[mh][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mh][s], qf[nb][s], st[mh][nb], 0, 0, 0);
+      };
+      // With two row blocks the logits of both halves are issued first: each half's softmax then
+      // runs on the VALU while the matrix cores still work on the other half's logits (or the
+      // previous PV).  With four row blocks the registers allow only one half at a time.
+      constexpr int LIVE = NB <= 2 ? 2 : 1;
+      f32x4 st2[LIVE][2][NB];
+      if constexpr (LIVE == 2) {
+        logits(0, st2[0]);
+        logits(1, st2[1]);
+      }
 #pragma unroll
-          for (int s = 0; s < NKS; ++s)
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (LIVE == 1) logits(ks, st2[0]);
+        f32x4 (&st)[2][NB] = st2[LIVE == 2 ? ks : 0];
+        if (!clean) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const RowMask rm = row_mask(row_ok[nb], qpos[nb], kv_hi, a.causal, a.window, a.sink);
 #pragma unroll
             for (int mh = 0; mh < 2; ++mh)
-              kf[mh][s] = *reinterpret_cast<const bf16x8*>(sk + 16 * (2 * ks + mh) * D + k_rd +
-                                                           8 * ((4 * s + j) ^ k_sw));
 #pragma unroll
-          for (int s = 0; s < NKS; ++s)
+              for (int i = 0; i < 4; ++i)
+                st[mh][nb][i] = row_sees(rm, kt + 16 * (2 * ks + mh) + 4 * j + i) ? st[mh][nb][i] : -INFINITY;
+          }
+        }
+        // Online softmax with a lazily moved reference: each lane checks its own logits against
+        // the row's threshold; only if some lane exceeds it is the row max reduced across the
+        // row's four lanes and the state rescaled.
+        float lmax[NB];
+        uint64_t grow = 0;
 #pragma unroll
-            for (int mh = 0; mh < 2; ++mh)
+        for (int nb = 0; nb < NB; ++nb) {
+          float x = fmaxf(fmaxf(st[0][nb][0], st[0][nb][1]), st[0][nb][2]);
+          x = fmaxf(fmaxf(x, st[0][nb][3]), st[1][nb][0]);
+          x = fmaxf(fmaxf(x, st[1][nb][1]), st[1][nb][2]);
+          lmax[nb] = fmaxf(x, st[1][nb][3]);
+          grow |= __builtin_amdgcn_ballot_w64(lmax[nb] > thr[nb]);
+        }
+        if (grow) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const float bm = wave_max_xor16_32(lmax[nb]) * a.scale_log2;  // scale > 0 keeps the max
+            if (bm > m_run[nb] + kPreRescaleSlack) {
+              const float alpha = m_run[nb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - bm);
+              l_run[nb] *= alpha;
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) acc[nb][db] *= alpha;
+              m_run[nb] = bm;
+              neg_m[nb] = -bm;
+              thr[nb] = (bm + kPreRescaleSlack) * inv_scale_log2;
+            }
+          }
+        }
+        // P (bf16 operand of the PV product) and the row sums
+        bf16x8 pb[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          u32x4 pw;
+          float pr[2][4];
+#pragma unroll
+          for (int mh = 0; mh < 2; ++mh) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pr[mh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mh][nb][i], a.scale_log2, neg_m[nb]));
+            // MFMA k elements 0..3 hold key block 2ks, elements 4..7 block 2ks+1
+            pw[2 * mh] = pack_bf16x2(pr[mh][0], pr[mh][1]);
+            pw[2 * mh + 1] = pack_bf16x2(pr[mh][2], pr[mh][3]);
+          }
+          pb[nb] = __builtin_bit_cast(bf16x8, pw);
+          // the row sum adds the fp32 values: the log-sum-exp keeps their precision
+          l_run[nb] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
+        }
+
+        // O^T[d][row] += V^T P^T.  MFMA k index 8j+e <-> key 32ks + 4j + (e&3) + 16(e>>2): the
+        // keys whose probabilities this lane holds.  The V^T operand comes from two transposing
+        // LDS reads: in each 16-lane group, lane k points at 4 columns of key row k/4 and gets
+        // back one column of 4 keys, so lane (n, j) receives V[key(8j+e)][16 db + n].
+        {
+          const unsigned short* vb = sv + (32 * ks + v_row) * D + v_half;
+          constexpr int VB = NB <= 2 ? NDB : 2;  // V^T operands read ahead of their MFMAs
+#pragma unroll
+          for (int d0 = 0; d0 < NDB; d0 += VB) {
+            bf16x8 va[VB];
+#pragma unroll
+            for (int i = 0; i < VB; ++i) {
+              const int off = 8 * ((2 * (d0 + i) + ((n & 3) >> 1)) ^ v_sw);
+              va[i] = ds_read_tr_pair(vb + off, vb + off + 16 * D);
+            }
+#pragma unroll
+            for (int i = 0; i < VB; ++i)
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb)
-                st[mh][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mh][s], qf[nb][s], st[mh][nb], 0, 0, 0);
-        };
-        // With two row blocks the logits of both halves are issued first: each half's softmax then
-        // runs on the VALU while the matrix cores still work on the other half's logits (or the
-        // previous PV).  With four row blocks the registers allow only one half at a time.
-        constexpr int LIVE = NB <= 2 ? 2 : 1;
-        f32x4 st2[LIVE][2][NB];
-        if constexpr (LIVE == 2) {
-          logits(0, st2[0]);
-          logits(1, st2[1]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if constexpr (LIVE == 1) logits(ks, st2[0]);
-          f32x4 (&st)[2][NB] = st2[LIVE == 2 ? ks : 0];
-          if (!clean) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const RowMask rm = row_mask(row_ok[nb], qpos[nb], kv_hi, a.causal, a.window, a.sink);
-#pragma unroll
-              for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  st[mh][nb][i] = row_sees(rm, kt + 16 * (2 * ks + mh) + 4 * j + i) ? st[mh][nb][i] : -INFINITY;
-            }
-          }
-          // Online softmax with a lazily moved reference: each lane checks its own logits against
-          // the row's reference plus the slack; only if some lane exceeds it is the row max
-          // reduced across the row's four lanes and the state rescaled.
-          float lmax[NB];
-          bool grow = false;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            lmax[nb] = fmaxf(fmaxf(fmaxf(st[0][nb][0], st[0][nb][1]), fmaxf(st[0][nb][2], st[0][nb][3])),
-                             fmaxf(fmaxf(st[1][nb][0], st[1][nb][1]), fmaxf(st[1][nb][2], st[1][nb][3])));
-            grow = grow || lmax[nb] * a.scale_log2 > m_run[nb] + kPreRescaleSlack;
-          }
-          if (__any(grow)) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const float bm = wave_max_xor16_32(lmax[nb]) * a.scale_log2;  // scale > 0 keeps the max
-              if (bm > m_run[nb] + kPreRescaleSlack) {
-                const float alpha = m_run[nb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - bm);
-                l_run[nb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[nb][db] *= alpha;
-                m_run[nb] = bm;
-              }
-            }
-          }
-          bf16x8 pb[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float neg_m = m_run[nb] == -INFINITY ? 0.f : -m_run[nb];
-            float psum = 0.f;
-            u32x4 pw;
-#pragma unroll
-            for (int mh = 0; mh < 2; ++mh) {
-              float pr[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mh][nb][i], a.scale_log2, neg_m));
-                psum += pr[i];
-              }
-              // MFMA k elements 0..3 hold key block 2ks, elements 4..7 block 2ks+1
-              pw[2 * mh] = pack_bf16x2(pr[0], pr[1]);
-              pw[2 * mh + 1] = pack_bf16x2(pr[2], pr[3]);
-            }
-            pb[nb] = __builtin_bit_cast(bf16x8, pw);
-            l_run[nb] += psum;
-          }
-
-          // O^T[d][row] += V^T P^T.  MFMA k index 8j+e <-> key 32ks + 4j + (e&3) + 16(e>>2): the
-          // keys whose probabilities this lane holds.  The V^T operand comes from two transposing
-          // LDS reads: in each 16-lane group, lane k points at 4 columns of key row k/4 and gets
-          // back one column of 4 keys, so lane (n, j) receives V[key(8j+e)][16 db + n].
-          {
-            const unsigned short* vb = sv + (32 * ks + v_row) * D + v_half;
-            constexpr int VB = NB <= 2 ? NDB : 2;  // V^T operands read ahead of their MFMAs
-#pragma unroll
-            for (int d0 = 0; d0 < NDB; d0 += VB) {
-              bf16x8 va[VB];
-#pragma unroll
-              for (int i = 0; i < VB; ++i) {
-                const int off = 8 * ((2 * (d0 + i) + ((n & 3) >> 1)) ^ v_sw);
-                va[i] = ds_read_tr_pair(vb + off, vb + off + 16 * D);
-              }
-#pragma unroll
-              for (int i = 0; i < VB; ++i)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                  acc[nb][d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pb[nb], acc[nb][d0 + i], 0, 0, 0);
-            }
+                acc[nb][d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pb[nb], acc[nb][d0 + i], 0, 0, 0);
           }
         }
       }
+    };
+
+    wait_vm();  // q fragments and page ids are in registers before the tile loop starts
+    if (ntiles > 0) load_tile(kv_lo, 0);
+    // two tiles per iteration, one from each LDS buffer; every wave passes the same barriers
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      tile_step(tile, Const<int, 0>{});
+      if (tile + 1 < ntiles) tile_step(tile + 1, Const<int, 1>{});
     }
 
     // epilogue: each lane owns row n of each row block and columns 16 db + 4 j .. + 3
