@@ -226,7 +226,7 @@ bsk_status bsk_device_workers(const bsk_problem* problem, int32_t* num_workers) 
                ? bsk::mixed_kernel_ptr(problem->head_dim, problem->independent_kv_strides == 0)
                : bsk::prefill_kernel_ptr(problem->head_dim, dense, problem->tile_q,
                                          problem->independent_kv_strides == 0);
-    threads = bsk::prefill_threads();
+    threads = problem->decode_tile_q != 0 ? bsk::prefill_threads(128) : bsk::prefill_threads(problem->tile_q);
   } else {
     return fail(BSK_ERR_INVALID_ARG, "tile_q must be 16, 128 or 256");
   }

@@ -15,7 +15,7 @@ int decode_threads();
 hipError_t launch_prefill(int head_dim, bool dense, int tile_q, bool same, const AttnArgs& a, int grid,
                           hipStream_t stream);
 const void* prefill_kernel_ptr(int head_dim, bool dense, int tile_q, bool same);
-int prefill_threads();
+int prefill_threads(int tile_q);
 
 hipError_t launch_mixed(int head_dim, bool same, const AttnArgs& a, int grid, hipStream_t stream);
 const void* mixed_kernel_ptr(int head_dim, bool same);
