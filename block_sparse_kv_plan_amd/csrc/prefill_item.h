@@ -26,10 +26,11 @@
 //   whose probabilities the lane already holds
 // and every wave writes its own rows (output or partial state).
 //
-// Every K/V tile read from LDS is shared by all NB row blocks of a wave, so
-// NB = 4 (64 rows per wave, one workgroup per CU with up to 512 registers
-// per lane) halves the LDS reads, V repacks and address work per MFMA
-// relative to NB = 2 (32 rows per wave, two workgroups per CU).
+// Every K/V tile read from LDS is shared by all NB row blocks of a wave.  The
+// kernels use NB = 2 (32 rows per wave, two workgroups per CU, so that the two
+// waves of a SIMD overlap one's MFMAs with the other's softmax); NB = 4 (64
+// rows per wave, one wave per SIMD) halves the LDS reads per MFMA but loses
+// that overlap and was slower.  256-row items use prefill_pp_item.h.
 //
 // The logit max uses fmaxf on values that are never NaN (masked logits are
 // replaced by -inf before it), so the files that include this one are built
