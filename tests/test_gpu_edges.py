@@ -29,7 +29,10 @@ def test_decode_long_sequence_at_chunk_capacity(ps):
     compare(b, O, L)
 
 
-@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL])
+ALL_TILES = [bsk.TILE_DECODE, bsk.TILE_PREFILL, bsk.TILE_PREFILL_256]
+
+
+@pytest.mark.parametrize("tile_q", ALL_TILES)
 @pytest.mark.parametrize("window,sink", [(1, 0), (1, 3), (2, 1)])
 def test_tiny_windows(tile_q, window, sink):
     """A window of one or two keys, with or without sinks: a query sees itself (and its
@@ -42,7 +45,7 @@ def test_tiny_windows(tile_q, window, sink):
     compare(b, O, L)
 
 
-@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL])
+@pytest.mark.parametrize("tile_q", ALL_TILES)
 def test_sinks_past_the_window_start_and_wide_windows(tile_q):
     """sink larger than the window start (the sink range stops at the window) and windows wider
     than the sequence (no effect)."""
@@ -71,7 +74,7 @@ def test_noncausal_prefill_group_of_one():
     compare(b, O, L)
 
 
-@pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL])
+@pytest.mark.parametrize("tile_q", ALL_TILES)
 def test_almost_all_requests_empty(tile_q):
     """Nine empty requests around one real one, and a batch whose only request has one key."""
     kv = [0] * 4 + [777] + [0] * 5
@@ -82,3 +85,18 @@ def test_almost_all_requests_empty(tile_q):
     b1 = batch(333, [1], qo=[1], Hq=8, Hk=2, causal=True)
     O, L, _, _ = run(b1, tile_q=tile_q, num_workers=16)
     compare(b1, O, L)
+
+
+@pytest.mark.parametrize("tile_q", [bsk.TILE_PREFILL, bsk.TILE_PREFILL_256])
+@pytest.mark.parametrize("indep", [0, 1])
+def test_head_dim_64_window_sink_split_chunks(tile_q, indep):
+    """d = 64 with a sliding window, sinks and chunks split over several workers (merged), both
+    K/V stride modes; rows past the last 256-row tile's end and a key range that starts inside
+    a tile."""
+    kv = [700, 1500, 90, 2100]
+    qo = [300, 70, 90, 513]
+    b = batch(340 + indep, kv, qo=qo, Hq=16, Hk=4, d=64, ps=8, causal=True, window=333, sink=5)
+    say(f"d64 window+sink tile_q={tile_q} indep={indep}")
+    O, L, attn, _ = run(b, tile_q=tile_q, num_workers=40, split_factor=3, min_chunk=128, independent_kv_strides=indep)
+    assert attn.info.num_merge > 0
+    compare(b, O, L)
