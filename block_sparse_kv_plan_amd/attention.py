@@ -103,6 +103,7 @@ class BatchAttention:
         self._merged = torch.cuda.Event()     # the last merge reading int_ws / float_ws has completed
         self._consumed_stream = None
         self._merged_stream = None
+        self._run_stream = None  # stream of a run(merge=False) whose merge() has not been called yet
         self._upload_pending = False
         self._upload_stream = None
 
@@ -117,6 +118,7 @@ class BatchAttention:
             self._uploaded.synchronize()  # host_ws is still being read by the previous copy
         stream = stream or torch.cuda.current_stream(self.device)
         up = copy_stream if copy_stream is not None else stream
+        self._settle_run()
         # do not overwrite int_ws under a kernel that still reads it on another stream: wait for the
         # last run and the last merge (one wait when both went to the same stream, the merge last)
         waits = []
@@ -145,21 +147,34 @@ class BatchAttention:
             run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         else:
             run_prefill(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
-        self._consumed.record(stream)
-        self._consumed_stream = stream
+        self._consumed_stream = None
         self._merged_stream = None  # the last merge event belongs to an earlier run
+        # The merge that follows (on this stream, or on one the caller made wait for this run) ends
+        # after the run, so its event also covers the run; the run's own event -- a packet on the
+        # queue that costs microseconds -- is recorded only if no merge comes (_settle_run).
+        self._run_stream = stream
         if merge:
             self.merge(tensors, stream)
+
+    def _settle_run(self):
+        """Record the consumed event of a run whose merge was never called (conservatively: after
+        everything queued on the run's stream so far)."""
+        if self._run_stream is not None:
+            self._consumed.record(self._run_stream)
+            self._consumed_stream = self._run_stream
+            self._run_stream = None
 
     def merge(self, tensors: Tensors, stream=None):
         """The split-KV merge of the last run (nothing when the run merged in-kernel).  On another
         stream than the run's, the caller makes that stream wait for the run first."""
         if self.problem.fused_merge:
+            self._settle_run()
             return
         stream = stream or torch.cuda.current_stream(self.device)
         merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         self._merged.record(stream)
         self._merged_stream = stream
+        self._run_stream = None
 
 
 def merge_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):

@@ -364,10 +364,11 @@ bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* inf
   a.lse_st = t->lse_stride_tok;
   a.group = problem->num_qo_heads / problem->num_kv_heads;
   a.out_bf16 = problem->out_dtype == BSK_DTYPE_BF16;
-  // fixed grid: enough blocks for every (entry, row) pair of a full merge table, capped
+  // fixed grid: enough blocks for every (entry, row) pair of a full merge table, capped at four
+  // per compute unit (the blocks loop; idle blocks only cost their dispatch)
   const int64_t rows_per_block = 256 / (problem->head_dim / 4);
   const int64_t want = (int64_t(problem->max_merge) * problem->tile_q + rows_per_block - 1) / rows_per_block;
-  const int grid = int(want < 1 ? 1 : (want > 4096 ? 4096 : want));
+  const int grid = int(want < 1 ? 1 : (want > 1024 ? 1024 : want));
   hipError_t e = bsk::launch_merge(problem->head_dim, a, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return BSK_OK;

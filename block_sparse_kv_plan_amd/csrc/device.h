@@ -48,29 +48,44 @@ __device__ __forceinline__ void merge_row(const int32_t* rec, int rr, int c4, in
   const int first = rec[MG_FIRST_SLOT], nc = rec[MG_N];
   const float* pl = part_lse + int64_t(first) * tile_q + rr;
   const float* po = part_o + (int64_t(first) * tile_q + rr) * D + c4;
-  // one pass with a running max (the loads of different chunks are independent)
+  // chunks in groups of eight: all loads of a group are issued together (one memory latency per
+  // group), then the group's maximum moves the running reference and its terms are added
   float M = -INFINITY, wsum = 0.f;
   float4 o = {0, 0, 0, 0};
-#pragma unroll 4
-  for (int c = 0; c < nc; ++c) {
-    const float lc = pl[int64_t(c) * tile_q];
-    const float4 x = *reinterpret_cast<const float4*>(po + int64_t(c) * tile_q * D);
-    if (lc > M) {
-      const float sc = __expf(M - lc);  // 0 when M was -inf
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    float lc[8];
+    float4 x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      // past the last chunk: the last chunk's values are read again (always in bounds, so the
+      // loads need no predicate) and weighted 0
+      const int c = min(c0 + k, nc - 1);
+      const float l = pl[int64_t(c) * tile_q];
+      lc[k] = c0 + k < nc ? l : -INFINITY;
+      x[k] = *reinterpret_cast<const float4*>(po + int64_t(c) * tile_q * D);
+    }
+    float gm = lc[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) gm = fmaxf(gm, lc[k]);
+    if (gm > M) {
+      const float sc = __expf(M - gm);  // 0 while M is still -inf
       o.x *= sc;
       o.y *= sc;
       o.z *= sc;
       o.w *= sc;
       wsum *= sc;
-      M = lc;
+      M = gm;
     }
-    if (lc != -INFINITY) {
-      const float w = __expf(lc - M);
-      o.x += w * x.x;
-      o.y += w * x.y;
-      o.z += w * x.z;
-      o.w += w * x.w;
-      wsum += w;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = lc[k] == -INFINITY ? 0.f : __expf(lc[k] - M);  // an empty chunk holds O = 0
+        o.x += w * x[k].x;
+        o.y += w * x[k].y;
+        o.z += w * x[k].z;
+        o.w += w * x[k].w;
+        wsum += w;
+      }
     }
   }
   float lse = -INFINITY;

@@ -18,7 +18,9 @@ constexpr int kMergeThreads = 256;
 
 // Plan-driven merge: fixed grid.  Work is spread over (merge entry, row)
 // pairs -- D/4 threads per row, each owning four columns -- so a few long
-// entries (a prefix split into many chunks) still use the whole chip.
+// entries (a prefix split into many chunks) still use the whole chip.  No
+// entry has more rows than min(tile_q, longest query * group): decode entries
+// (one token, a GQA group of rows) then take no idle threads.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int TPR = D / 4;                  // threads per row
@@ -26,14 +28,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int32_t* __restrict__ ws = a.ws;
   const int n_merge = ws[HDR_NUM_MERGE];
   const int tile_q = ws[HDR_TILE_Q];
+  const int rows = int(min(int64_t(tile_q), int64_t(ws[HDR_MAX_QO_LEN]) * a.group));
   const int32_t* __restrict__ table = ws + ws[HDR_OFF_MERGE];
   const int32_t* __restrict__ qo_indptr = ws + ws[HDR_OFF_QO];
   const int g = a.group;
   const int c4 = (threadIdx.x % TPR) * 4;
-  const int64_t n_virtual = int64_t(n_merge) * tile_q;  // (entry, row-in-tile) pairs
+  const int64_t n_virtual = int64_t(n_merge) * rows;  // (entry, row) pairs
   for (int64_t v = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR; v < n_virtual; v += int64_t(gridDim.x) * RPB) {
-    const int m = int(v / tile_q);
-    const int rr = int(v % tile_q);
+    const int m = int(v / rows);
+    const int rr = int(v % rows);
     const int32_t* rec = table + int64_t(m) * MERGE_WORDS;
     if (rr >= rec[MG_ROW_HI] - rec[MG_ROW_LO]) continue;
     merge_row<D>(rec, rr, c4, tile_q, a.part_o, a.part_lse, qo_indptr[rec[MG_R]], g, a.out, a.o_st, a.o_sh, a.lse,
