@@ -51,10 +51,9 @@ constexpr float kRescaleSlack = 8.f;  // log2 units: rescale only when the max g
 enum : int { ROPE_NONE = 0, ROPE_STREAMING = 1, ROPE_ABSOLUTE = 2 };
 
 // Rotate-half RoPE on a lane's fragment pair: lo holds elements k..k+7 of
-// the first half, hi the matching k+D/2.. elements; cs points at the (cos,
-// sin) pairs of k..k+7 for the position.
-__device__ __forceinline__ void rope8(float* lo, float* hi, const float* __restrict__ cs) {
-  const float4* c4 = reinterpret_cast<const float4*>(cs);
+// the first half, hi the matching k+D/2.. elements; c4 holds the (cos, sin)
+// pairs of k..k+7 for the position.
+__device__ __forceinline__ void rope8(float* lo, float* hi, const float4* c4) {
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
     const float4 t = c4[e2];  // cos_e, sin_e, cos_e+1, sin_e+1
@@ -133,6 +132,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same value, known to be uniform
   const int n = lane & 15;  // MFMA N index: this lane's query row
   const int j = lane >> 4;  // lane group
   // key row (within a 16-key block) this lane feeds to the logits MFMA
@@ -189,7 +189,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
           float lo[8], hi[8];
           unpack_bf16x8(qh[s], lo);
           unpack_bf16x8(qh[s + HALF_KS], hi);
-          rope8(lo, hi, a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2);
+          rope8(lo, hi, reinterpret_cast<const float4*>(a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2));
           qr[s] = to_f16x8(lo);
           qr[s + HALF_KS] = to_f16x8(hi);
         }
@@ -277,23 +277,37 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
         }
       };
 
-      auto compute_block = [&](int b, bf16x8* kf, const u32x4* vf) {
+      // (cos, sin) pairs of this lane's key row for the frequencies of its fragments 4s + j
+      // (s < HALF_KS): four float4 per fragment
+      constexpr int NCS = ROPE == ROPE_NONE ? 1 : 4 * HALF_KS;
+      auto load_table = [&](int b, float4* cs) {
+        if constexpr (ROPE != ROPE_NONE) {
+          const int tk = min(max(((blk0 + b) << 4) + kkey, kmin), kmax);
+          int pk = ROPE == ROPE_STREAMING ? (tk < n_s ? tk : n_s + (tk - lo_w)) : tk;
+          pk = min(max(pk, 0), a.rope_n_pos - 1);
+#pragma unroll
+          for (int s = 0; s < HALF_KS; ++s) {
+            const float4* c4 = reinterpret_cast<const float4*>(a.rope + (int64_t(pk) * (D / 2) + 8 * (4 * s + j)) * 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cs[4 * s + e] = c4[e];
+          }
+        }
+      };
+
+      auto compute_block = [&](int b, bf16x8* kf, const u32x4* vf, const float4* cs) {
         const int tb = (blk0 + b) << 4;
         f32x4 st = {0, 0, 0, 0};
         if constexpr (ROPE == ROPE_NONE) {
 #pragma unroll
           for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
         } else {
-          const int tk = min(max(tb + kkey, kmin), kmax);
-          int pk = ROPE == ROPE_STREAMING ? (tk < n_s ? tk : n_s + (tk - lo_w)) : tk;
-          pk = min(max(pk, 0), a.rope_n_pos - 1);
           f16x8 kr[NKS];
 #pragma unroll
           for (int s = 0; s < HALF_KS; ++s) {
             float lo[8], hi[8];
             unpack_bf16x8(kf[s], lo);
             unpack_bf16x8(kf[s + HALF_KS], hi);
-            rope8(lo, hi, a.rope + (int64_t(pk) * (D / 2) + 8 * (4 * s + j)) * 2);
+            rope8(lo, hi, &cs[4 * s]);
             kr[s] = to_f16x8(lo);
             kr[s + HALF_KS] = to_f16x8(hi);
           }
@@ -319,19 +333,27 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
                                                               0, 0, 0);
       };
 
-      // two register sets: the next block's loads are in flight while the current one is consumed
+      // Two register sets: the next block's loads are in flight while the current one is consumed.
+      // Every iteration issues the same loads in the same order -- a wave without a next block
+      // reads its current block again (an L2 hit) -- so the wait before a block's math only has
+      // to let the next block's loads (and, with RoPE, nothing else) stay outstanding; a load
+      // skipped on some path would force a wait for everything issued so far.  The RoPE table
+      // values of a block are requested before the next block's K/V for the same reason.
       bf16x8 ka[NKS], kb2[NKS];
       u32x4 va[4], vb2[4];
-      int b = wave;
+      float4 cs[NCS];
+      int b = wave_u;
       if (b < nblk) load_block(b, ka, va);
       for (; b < nblk; b += 2 * kDecWaves) {
         const int b1 = b + kDecWaves;
-        if (b1 < nblk) load_block(b1, kb2, vb2);
-        compute_block(b, ka, va);
+        load_table(b, cs);
+        load_block(b1 < nblk ? b1 : b, kb2, vb2);
+        compute_block(b, ka, va, cs);
         if (b1 >= nblk) break;
         const int b2 = b1 + kDecWaves;
-        if (b2 < nblk) load_block(b2, ka, va);
-        compute_block(b1, kb2, vb2);
+        load_table(b1, cs);
+        load_block(b2 < nblk ? b2 : b1, ka, va);
+        compute_block(b1, kb2, vb2, cs);
       }
     } else {
       for (int b = wave; b < nblk; b += kDecWaves) {
