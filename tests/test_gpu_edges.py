@@ -100,3 +100,21 @@ def test_head_dim_64_window_sink_split_chunks(tile_q, indep):
     O, L, attn, _ = run(b, tile_q=tile_q, num_workers=40, split_factor=3, min_chunk=128, independent_kv_strides=indep)
     assert attn.info.num_merge > 0
     compare(b, O, L)
+
+
+@pytest.mark.parametrize("tile_q", ALL_TILES)
+def test_units_split_into_many_chunks(tile_q):
+    """Units cut into 20-30 chunks of 64 keys: the merge reads the chunks of a row in groups of
+    eight, so its running reference moves between groups, and with causal prefill rows the
+    last chunks hold no visible key for the unit's first rows (partial LSE = -inf).  The
+    in-kernel merge gives the same bits."""
+    qo = [1, 1, 1] if tile_q == bsk.TILE_DECODE else [40, 130, 3]
+    kv = [1500, 1100, 37] if tile_q == bsk.TILE_DECODE else [1500, 1100, 37]
+    b = batch(330, kv, qo=qo, Hq=8, Hk=2, causal=True)
+    say(f"many chunks tile_q={tile_q}")
+    O1, L1, attn, _ = run(b, tile_q=tile_q, num_workers=8, split_factor=64, min_chunk=64, fused_merge=0)
+    assert attn.info.chunk == 64 and attn.info.num_merge >= 2
+    assert attn.info.num_slots >= 9 * attn.info.num_merge  # more than one group of eight per unit on average
+    compare(b, O1, L1)
+    O2, L2, _, _ = run(b, tile_q=tile_q, num_workers=8, split_factor=64, min_chunk=64, fused_merge=1)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
