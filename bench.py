@@ -144,13 +144,13 @@ def timed(runner, steps, warmup):
     """Wall time per step over `steps` back-to-back steps, and the attention kernel's and the
     merge's mean durations from events on their launch stream.  Plans are uploaded on a copy
     stream (off the kernels' queue; a third stream for the merges measured slower); the
-    kernel / merge events are recorded on every fourth
-    timed step (every step when there are fewer than 80), since each event is a packet on the
-    kernels' queue and costs a few microseconds of its own."""
+    kernel / merge events are recorded on every eighth timed step (every fourth below 160 steps,
+    every step below 80), since each event is a packet on the kernels' queue and costs about
+    3 microseconds of its own."""
     import torch
     stream = torch.cuda.current_stream()
     copy_stream = torch.cuda.Stream()
-    every = 4 if steps >= 80 else 1
+    every = 8 if steps >= 160 else (4 if steps >= 80 else 1)
     for i in range(warmup):
         runner.step(i, stream, copy_stream=copy_stream)
     torch.cuda.synchronize()
@@ -354,7 +354,7 @@ def mixed_leg(device, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
