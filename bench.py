@@ -365,6 +365,9 @@ def main():
     ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
     ap.add_argument("--decode-min-chunk", type=int, default=None, help="plan min_chunk (keys) of the decode workload")
     ap.add_argument("--decode-overhead", type=int, default=None, help="plan item_overhead (keys) of the decode workload")
+    ap.add_argument("--fused-merge", type=int, choices=(0, 1), default=None,
+                    help="merge split units in-kernel (1) or with the separate merge kernel (0) on the decode-class "
+                         "workloads (Llama-3 decode, streaming RoPE decode)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
@@ -397,7 +400,8 @@ def main():
         b = W.llama3_decode()
         nbytes = decode_bytes(b)
         dkw = {k: v for k, v in (("split_factor", args.decode_split), ("min_chunk", args.decode_min_chunk),
-                                  ("item_overhead", args.decode_overhead)) if v is not None}
+                                  ("item_overhead", args.decode_overhead), ("fused_merge", args.fused_merge))
+               if v is not None}
         runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device, **dkw)
         log(f"decode: {int(b.kv_len.sum())} keys, {nbytes / 1e9:.3f} GB per step; timing {args.steps} steps")
         m = timed(runner, args.steps, args.warmup)
@@ -544,7 +548,8 @@ def main():
         log("rope: long-context streaming decode with fused RoPE, window 4096 + 4 sinks")
         b = W.streaming_rope_decode()
         nbytes = decode_bytes(b)
-        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device)
+        rkw = {} if args.fused_merge is None else {"fused_merge": args.fused_merge}
+        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, **rkw)
         m = timed(runner, args.steps, args.warmup)
         secondary["streaming_rope_decode"] = {
             "workload": "streaming_rope_window_sink_decode_bf16: batch 8, kv uniform [32768,131072], 64q/8kv, "

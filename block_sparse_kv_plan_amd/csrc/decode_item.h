@@ -460,8 +460,8 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
         }
         if (c4 == 0) a.lse[int64_t(tok) * a.lse_st + qhd] = lse;
       } else {
-        *reinterpret_cast<float4*>(a.part_o + (int64_t(slot) * part_rows + rr) * D + c4) = o;
-        if (c4 == 0) a.part_lse[int64_t(slot) * part_rows + rr] = lse;
+        store_part4(a.part_o + (int64_t(slot) * part_rows + rr) * D + c4, o.x, o.y, o.z, o.w, a.fused_merge);
+        if (c4 == 0) store_part(a.part_lse + int64_t(slot) * part_rows + rr, lse, a.fused_merge);
       }
     }
     if (slot >= 0 && a.fused_merge) finish_split_chunk<D>(a, slot, tid, kDecThreads, s_last);

@@ -35,11 +35,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Partial states exchanged inside one launch (the in-kernel merge) pass between workgroups that
+// may run on different XCDs, whose L2 caches are not coherent with each other.  They are stored
+// and loaded as relaxed device-scope atomics (cache-coherent accesses at the device's coherence
+// point), so publishing them needs only the wait for the stores to complete -- no L2 writeback
+// or invalidation.  Without the in-kernel merge they are plain accesses.
+__device__ __forceinline__ void store_part(float* p, float v, bool coherent) {
+  if (coherent)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+__device__ __forceinline__ void store_part4(float* p, float x, float y, float z, float w, bool coherent) {
+  if (coherent) {
+    store_part(p, x, true);
+    store_part(p + 1, y, true);
+    store_part(p + 2, z, true);
+    store_part(p + 3, w, true);
+  } else {
+    *reinterpret_cast<float4*>(p) = float4{x, y, z, w};
+  }
+}
+template <bool COHERENT>
+__device__ __forceinline__ float load_part(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <bool COHERENT>
+__device__ __forceinline__ float4 load_part4(const float* p) {
+  if constexpr (COHERENT)
+    return float4{load_part<true>(p), load_part<true>(p + 1), load_part<true>(p + 2), load_part<true>(p + 3)};
+  else
+    return *reinterpret_cast<const float4*>(p);
+}
+
 // Merge of one (row, 4 columns) of a split unit from its chunks' partial
 // states: M = max_c LSE_c, w_c = exp(LSE_c - M), O = sum_c w_c O_c / sum_c w_c,
 // LSE = M + ln sum_c w_c; every chunk empty gives O = 0, LSE = -inf.  Writes
 // the output row (and the LSE when c4 == 0).
-template <int D>
+template <int D, bool COHERENT = false>
 __device__ __forceinline__ void merge_row(const int32_t* rec, int rr, int c4, int tile_q,
                                           const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                           int q0, int g, void* out, int64_t o_st, int64_t o_sh, float* lse_out,
@@ -60,9 +96,9 @@ __device__ __forceinline__ void merge_row(const int32_t* rec, int rr, int c4, in
       // past the last chunk: the last chunk's values are read again (always in bounds, so the
       // loads need no predicate) and weighted 0
       const int c = min(c0 + k, nc - 1);
-      const float l = pl[int64_t(c) * tile_q];
+      const float l = load_part<COHERENT>(pl + int64_t(c) * tile_q);
       lc[k] = c0 + k < nc ? l : -INFINITY;
-      x[k] = *reinterpret_cast<const float4*>(po + int64_t(c) * tile_q * D);
+      x[k] = load_part4<COHERENT>(po + int64_t(c) * tile_q * D);
     }
     float gm = lc[0];
 #pragma unroll
@@ -118,7 +154,7 @@ template <int D>
 __device__ __forceinline__ void finish_split_chunk(const AttnArgs& a, int slot, int tid, int nthreads,
                                                    int* s_flag) {
   const int32_t* __restrict__ ws = a.ws;
-  __threadfence();  // release this workgroup's partial-state stores device-wide
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial-state stores have completed (device-coherent)
   __syncthreads();
   const int m = ws[ws[HDR_OFF_SLOTMAP] + slot];
   const int32_t* rec = ws + ws[HDR_OFF_MERGE] + int64_t(m) * MERGE_WORDS;
@@ -131,13 +167,13 @@ __device__ __forceinline__ void finish_split_chunk(const AttnArgs& a, int slot, 
   }
   __syncthreads();
   if (*s_flag) {
-    __threadfence();  // acquire: the other chunks' partial states are visible
+    // the other chunks' partial states are read with device-coherent loads, issued only now
     const int tile_q = ws[HDR_TILE_Q];
     const int q0 = (ws + ws[HDR_OFF_QO])[rec[MG_R]];
     const int nrows = rec[MG_ROW_HI] - rec[MG_ROW_LO];
     for (int e = tid; e < nrows * (D / 4); e += nthreads)
-      merge_row<D>(rec, e / (D / 4), (e % (D / 4)) * 4, tile_q, a.part_o, a.part_lse, q0, a.group, a.out, a.o_st,
-                   a.o_sh, a.lse, a.lse_st, a.out_bf16);
+      merge_row<D, true>(rec, e / (D / 4), (e % (D / 4)) * 4, tile_q, a.part_o, a.part_lse, q0, a.group, a.out,
+                         a.o_st, a.o_sh, a.lse, a.lse_st, a.out_bf16);
   }
   __syncthreads();
 }

@@ -442,9 +442,12 @@ __device__ __forceinline__ void prefill_pp_item(const AttnArgs& a, const int32_t
       }
     } else {
       float* po = a.part_o + (int64_t(slot) * ROWS + rr) * D + 4 * j;
-      if (j == 0) a.part_lse[int64_t(slot) * ROWS + rr] = lse;
+      if (j == 0) store_part(a.part_lse + int64_t(slot) * ROWS + rr, lse, a.fused_merge);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = acc[nb][db] * inv;
+      for (int db = 0; db < NDB; ++db) {
+          const f32x4 v = acc[nb][db] * inv;
+          store_part4(po + 16 * db, v[0], v[1], v[2], v[3], a.fused_merge);
+        }
     }
   }
   if (slot >= 0 && a.fused_merge) finish_split_chunk<D>(a, slot, tid, kPPThreads, s_last);
