@@ -294,6 +294,35 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
         }
       };
 
+      // A wave's blocks are 4 x 16 keys apart, and inside an item the keys' positions are their
+      // indices plus a constant (streaming ranks included: an item lies entirely in the window or
+      // entirely in the sinks), so from the wave's third block on the (cos, sin) pairs follow from
+      // the previous block's by one rotation by 64 positions.  The first two blocks read the table:
+      // the first may hold keys before the item's range, whose positions are clamped.
+      float4 step[NCS];
+      if constexpr (ROPE != ROPE_NONE) {
+        const int p64 = min(4 * 16, a.rope_n_pos - 1);
+#pragma unroll
+        for (int s = 0; s < HALF_KS; ++s) {
+          const float4* c4 = reinterpret_cast<const float4*>(a.rope + (int64_t(p64) * (D / 2) + 8 * (4 * s + j)) * 2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) step[4 * s + e] = c4[e];
+        }
+      }
+      auto next_table = [&](int b, float4* cs) {
+        if constexpr (ROPE != ROPE_NONE) {
+          if (b - wave_u < 2 * kDecWaves) {
+            load_table(b, cs);
+          } else {
+#pragma unroll
+            for (int q = 0; q < NCS; ++q) {
+              const float4 c = cs[q], t = step[q];  // (cos, sin) of two frequencies
+              cs[q] = float4{c.x * t.x - c.y * t.y, c.y * t.x + c.x * t.y, c.z * t.z - c.w * t.w, c.w * t.z + c.z * t.w};
+            }
+          }
+        }
+      };
+
       auto compute_block = [&](int b, bf16x8* kf, const u32x4* vf, const float4* cs) {
         const int tb = (blk0 + b) << 4;
         f32x4 st = {0, 0, 0, 0};
@@ -346,12 +375,12 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
       if (b < nblk) load_block(b, ka, va);
       for (; b < nblk; b += 2 * kDecWaves) {
         const int b1 = b + kDecWaves;
-        load_table(b, cs);
+        next_table(b, cs);
         load_block(b1 < nblk ? b1 : b, kb2, vb2);
         compute_block(b, ka, va, cs);
         if (b1 >= nblk) break;
         const int b2 = b1 + kDecWaves;
-        load_table(b1, cs);
+        next_table(b1, cs);
         load_block(b2 < nblk ? b2 : b1, ka, va);
         compute_block(b1, kb2, vb2, cs);
       }
