@@ -296,9 +296,10 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 
       // A wave's blocks are 4 x 16 keys apart, and inside an item the keys' positions are their
       // indices plus a constant (streaming ranks included: an item lies entirely in the window or
-      // entirely in the sinks), so from the wave's third block on the (cos, sin) pairs follow from
-      // the previous block's by one rotation by 64 positions.  The first two blocks read the table:
-      // the first may hold keys before the item's range, whose positions are clamped.
+      // entirely in the sinks), so after the wave's first block the (cos, sin) pairs follow from
+      // the previous block's by one rotation by 64 positions.  The first block reads the table, and
+      // so does the second of wave 0 when the item starts inside a 16-key block: then wave 0's
+      // first block holds keys before the item's range, whose positions are clamped.
       float4 step[NCS];
       if constexpr (ROPE != ROPE_NONE) {
         const int p64 = min(4 * 16, a.rope_n_pos - 1);
@@ -311,7 +312,8 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
       }
       auto next_table = [&](int b, float4* cs) {
         if constexpr (ROPE != ROPE_NONE) {
-          if (b - wave_u < 2 * kDecWaves) {
+          const bool clamped_first = wave_u == 0 && (kv_lo & 15) != 0;
+          if (b - wave_u < (clamped_first ? 2 : 1) * kDecWaves) {
             load_table(b, cs);
           } else {
 #pragma unroll
