@@ -360,8 +360,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling aid: run just this workload (decode|prefill|append|strides|composable|rope|mixed|ceilings)")
-    ap.add_argument("--prefill-tile", type=int, default=128, choices=(128, 256),
-                    help="query-row tile of the prefill kernel (ragged prefill and the composable prefix)")
+    ap.add_argument("--prefill-tile", type=int, default=None, choices=(128, 256),
+                    help="query-row tile of the prefill kernel for both the ragged prefill and the composable "
+                         "prefix (default: 256 for the ragged prefill, 128 for the prefix)")
     ap.add_argument("--decode-split", type=int, default=None, help="plan split_factor of the decode workload")
     ap.add_argument("--decode-min-chunk", type=int, default=None, help="plan min_chunk (keys) of the decode workload")
     ap.add_argument("--decode-overhead", type=int, default=None, help="plan item_overhead (keys) of the decode workload")
@@ -372,6 +373,10 @@ def main():
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
     args = ap.parse_args()
+    # query-row tile of the ragged-prefill legs (256-row items: eight waves share each K/V tile)
+    # and of the composable's dense prefix (128-row items: twice the workers for 64 branch tokens)
+    prefill_tile = args.prefill_tile or 256
+    prefix_tile = args.prefill_tile or 128
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU "
               "path; run with --gpus 1", file=sys.stderr)
@@ -451,7 +456,7 @@ def main():
         log("prefill: ragged causal prefill with append")
         b = W.ragged_prefill()
         flops, pairs = prefill_flops(b)
-        runner = Runner(b, args.prefill_tile, copies=1, device=device)
+        runner = Runner(b, prefill_tile, copies=1, device=device)
         m = timed(runner, max(5, args.steps // 5), 3)
         tf = flops / m["kernel_s_mean"] / 1e12
         secondary["ragged_prefill"] = {
@@ -459,7 +464,7 @@ def main():
                         "uniform [0,2048] cached keys, 32q/8kv, d128",
             "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 1), "step_ms": round(m["wall_s"] * 1e3, 3),
-            "unmasked_pairs": pairs, "flops": flops, "tile_q": args.prefill_tile,
+            "unmasked_pairs": pairs, "flops": flops, "tile_q": prefill_tile,
             "num_workers": runner.attn[0].info.num_workers, "items": runner.attn[0].info.num_items}
         del runner
         torch.cuda.empty_cache()
@@ -504,7 +509,7 @@ def main():
         flops, _ = prefill_flops(b)
         attn = BatchAttention.create(device=device, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
                                      head_dim=b.head_dim, dtype=bsk.DTYPE_BF16, page_size=b.page_size, causal=True,
-                                     tile_q=args.prefill_tile, max_batch=b.batch_size)
+                                     tile_q=prefill_tile, max_batch=b.batch_size)
         out = torch.empty((T, b.num_qo_heads, b.head_dim), dtype=torch.float32, device=device)
         lse = torch.empty((T, b.num_qo_heads), dtype=torch.float32, device=device)
         chunk = 4096
@@ -520,7 +525,7 @@ def main():
         wall = (time.perf_counter() - t0) / reps
         secondary["chunked_prefill"] = {
             "workload": f"the ragged prefill run as steps of {chunk} new tokens (append + plan + prefill + merge "
-                        f"per step), tile_q {args.prefill_tile}",
+                        f"per step), tile_q {prefill_tile}",
             "steps": (T + chunk - 1) // chunk, "wall_ms": round(wall * 1e3, 3),
             "tflops_incl_host_steps": round(flops / wall / 1e12, 1)}
         del attn, du
@@ -530,7 +535,7 @@ def main():
         log("strides: equal-stride (shared address) kernels vs independent K/V stride kernels, same data")
         ab = {}
         for name, b, tq, copies in (("decode", W.llama3_decode(), bsk.TILE_DECODE, 4),
-                                    ("prefill", W.ragged_prefill(), args.prefill_tile, 1)):
+                                    ("prefill", W.ragged_prefill(), prefill_tile, 1)):
             us = []
             for ind in (0, 1):
                 runner = Runner(b, tq, copies=copies, device=device, independent_kv_strides=ind)
@@ -615,7 +620,7 @@ def main():
         for label, workers, side_stream in (("sequential", (None, None), None), ("concurrent", (cus, cus), side)):
             kw_p = {"num_workers": workers[0]} if workers[0] else {}
             kw_s = {"num_workers": workers[1]} if workers[1] else {}
-            pre = Runner(c.prefix, args.prefill_tile, copies=1, device=device, **kw_p)
+            pre = Runner(c.prefix, prefix_tile, copies=1, device=device, **kw_p)
             suf = Runner(c.suffix, bsk.TILE_DECODE, copies=1, device=device, **kw_s)
             fin_o = torch.empty_like(suf.out)
             fin_l = torch.empty_like(suf.lse)

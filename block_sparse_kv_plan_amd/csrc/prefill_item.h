@@ -8,8 +8,8 @@
 // kv head form one tile and read the prefix once.  Same persistent
 // plan-driven structure as the small-tile kernel; bf16 only.
 //
-// Per item (request r, kv head h, rows [row_lo, row_lo + 64 NB), keys
-// [kv_lo, kv_hi)): each of the four waves owns 16 NB rows (NB 16-row MFMA
+// Per item (request r, kv head h, rows [row_lo, row_lo + 16 NB WAVES), keys
+// [kv_lo, kv_hi)): each of the WAVES waves owns 16 NB rows (NB 16-row MFMA
 // column blocks) and the whole key range.  Keys go through LDS in 64-key
 // tiles, double-buffered, loaded by direct global-to-LDS transfers
 // (global_load_lds_dwordx4: every lane moves 16 bytes, a wave fills 1 KB
@@ -26,11 +26,12 @@
 //   whose probabilities the lane already holds
 // and every wave writes its own rows (output or partial state).
 //
-// Every K/V tile read from LDS is shared by all NB row blocks of a wave.  The
-// kernels use NB = 2 (32 rows per wave, two workgroups per CU, so that the two
-// waves of a SIMD overlap one's MFMAs with the other's softmax); NB = 4 (64
-// rows per wave, one wave per SIMD) halves the LDS reads per MFMA but loses
-// that overlap and was slower.  256-row items use prefill_pp_item.h.
+// Every K/V tile read from LDS is shared by all NB row blocks of a wave and by
+// all WAVES waves of the workgroup.  The kernels use NB = 2 (32 rows per wave)
+// with four waves (128-row items, two workgroups per CU) or eight waves
+// (256-row items, one workgroup per CU); either way a SIMD runs two waves, so
+// one's MFMAs overlap the other's softmax.  NB = 4 (64 rows per wave, one wave
+// per SIMD) halves the LDS reads per MFMA but loses that overlap and was slower.
 //
 // The logit max uses fmaxf on values that are never NaN (masked logits are
 // replaced by -inf before it), so the files that include this one are built
@@ -89,16 +90,17 @@ struct PrefillSmem {
 
 // SAME: K and V share page/head/token strides; a V address is the K address plus the K-to-V
 // pointer distance.
-template <int D, bool DENSE, int NB, bool SAME>
+template <int D, bool DENSE, int NB, bool SAME, int WAVES = kPreWaves>
 __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* __restrict__ rec, PrefillSmem<D>& sm,
                                              int32_t* s_pages, int* s_last) {
-  constexpr int ROWS = kPreWaves * 16 * NB;  // query rows per item (the plan's tile_q)
+  constexpr int ROWS = WAVES * 16 * NB;      // query rows per item (the plan's tile_q)
   constexpr int WROWS = 16 * NB;             // rows per wave
   constexpr int NDB = D / 16;                // 16-column blocks of the output
   constexpr int NKS = D / 32;                // k-steps over d for the logits
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int RPW = kWave / CH;            // key rows one wave-wide transfer fills (1 KB)
-  constexpr int NP = kPreKeys / (kPreWaves * RPW);  // transfers per wave per tile and tensor
+  constexpr int NP = kPreKeys / (WAVES * RPW);  // transfers per wave per tile and tensor
+  constexpr int NTHREADS = WAVES * kWave;
   constexpr int TILE = kPreKeys * D;         // bf16 per LDS tile
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(NB == 2 || NB == 4, "row blocks per wave");
@@ -130,7 +132,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
   int trow[NP], ck[NP], cv[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    trow[p] = (p * kPreWaves + wave) * RPW + lane / CH;
+    trow[p] = (p * WAVES + wave) * RPW + lane / CH;
     ck[p] = (lane % CH) ^ swz_k<D>(trow[p]);
     cv[p] = (lane % CH) ^ swz_v<D>(trow[p]);
   }
@@ -153,7 +155,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
     (void)r;
 
     __syncthreads();  // the previous item is done with the page list and the tiles
-    if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, kPreThreads);
+    if constexpr (!DENSE) stage_pages(s_pages, a.page_indices, kbase, kv_lo, kv_hi, a.page_shift, tid, NTHREADS);
     __syncthreads();
 
     // this lane's query rows (one per 16-row column block) and q fragments
@@ -224,7 +226,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
           const int64_t tv = 2 * (int64_t(kbase + kt) * a.v_st);
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+            const uint32_t lo = uint32_t((p * WAVES + wave_u) * 1024);
             const char* ka = kfix[p] + tk;
             dma16(ka, lk0 + lo);
             dma16(SAME ? ka + vdel[p] : vfix[p] + tv, lv0 + lo);
@@ -243,7 +245,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
             const int64_t tv = BIG ? 2 * (int64_t(kt & pmask) * a.v_st) : 0;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-              const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+              const uint32_t lo = uint32_t((p * WAVES + wave_u) * 1024);
               const char* ka = kfix[p] + uint64_t(page[p]) * k_page_bytes;
               if constexpr (BIG) ka += tk;
               dma16(ka, lk0 + lo);
@@ -269,7 +271,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
           const int64_t ko = kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.k_sp, a.k_sh, a.k_st);
           const int64_t vo =
               SAME ? ko : kv_offset<DENSE>(s_pages, t, kbase, kv_lo, a.page_shift, h, a.v_sp, a.v_sh, a.v_st);
-          const uint32_t lo = uint32_t((p * kPreWaves + wave_u) * 1024);
+          const uint32_t lo = uint32_t((p * WAVES + wave_u) * 1024);
           dma16(Kp + ko + 8 * ck[p], lk0 + lo);
           dma16(Vp + vo + 8 * cv[p], lv0 + lo);
         }
@@ -470,7 +472,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
         }
       }
     }
-    if (slot >= 0 && a.fused_merge) finish_split_chunk<D>(a, slot, tid, kPreThreads, s_last);
+    if (slot >= 0 && a.fused_merge) finish_split_chunk<D>(a, slot, tid, NTHREADS, s_last);
   }
 }
 

@@ -66,8 +66,8 @@ typedef int32_t bsk_status;
 
 #define BSK_TILE_DECODE 16       /* query-row tile of bsk_run_decode             */
 #define BSK_TILE_PREFILL 128     /* query-row tiles of bsk_run_prefill: 32 rows  */
-#define BSK_TILE_PREFILL_256 256 /* per wave (two workgroups per CU) or 64 rows  */
-                                 /* per wave (one workgroup per CU)             */
+#define BSK_TILE_PREFILL_256 256 /* per wave, four waves (two workgroups per CU) */
+                                 /* or eight (one workgroup per CU)             */
 
 /*
  * Problem description shared by plan, run and merge.  Query rows of a
