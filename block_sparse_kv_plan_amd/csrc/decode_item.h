@@ -249,6 +249,10 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 
     if constexpr (BF) {
       // K: this lane's key row kkey, pieces 4s + j.  V: keys 4i + j (i = 0..3), piece n % CHUNKS.
+      // Each V byte is read once, and one V load covers whole 128-byte lines (four full key rows),
+      // so the V loads carry the non-temporal hint and their lines do not linger in L2.  A K load
+      // covers half of each line it touches (four 16-byte pieces of a key row); the hint on K
+      // measured slower (a streamed line may leave L2 before its other half is read).
       auto load_block = [&](int b, bf16x8* kf, u32x4* vf) {
         const int tb = (blk0 + b) << 4;
         if (block_in_page) {
@@ -262,17 +266,19 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tv = min(max(tb + 4 * i + j, kmin), kmax);
-            vf[i] = *reinterpret_cast<const u32x4*>(Vp + vb + int64_t(tv - t0) * a.v_st + 8 * (n % CHUNKS));
+            vf[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(Vp + vb + int64_t(tv - t0) * a.v_st + 8 * (n % CHUNKS)));
           }
         } else {
           int64_t ko, vo;
           key_offsets(min(max(tb + kkey, kmin), kmax), ko, vo);
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(Kp + ko + 8 * (4 * s + j));
+          for (int s = 0; s < NKS; ++s)
+            kf[s] = *reinterpret_cast<const bf16x8*>(Kp + ko + 8 * (4 * s + j));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             key_offsets(min(max(tb + 4 * i + j, kmin), kmax), ko, vo);
-            vf[i] = *reinterpret_cast<const u32x4*>(Vp + vo + 8 * (n % CHUNKS));
+            vf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vp + vo + 8 * (n % CHUNKS)));
           }
         }
       };
