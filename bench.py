@@ -553,7 +553,11 @@ def main():
         log("rope: long-context streaming decode with fused RoPE, window 4096 + 4 sinks")
         b = W.streaming_rope_decode()
         nbytes = decode_bytes(b)
-        rkw = {} if args.fused_merge is None else {"fused_merge": args.fused_merge}
+        # Each unit sees 4100 keys (the window and the sinks).  Split factor 2 lets the 512-key chunk
+        # minimum bind: 512 keys are 32 blocks, eight for each of a worker's four waves, where the
+        # default's 528-key chunks give one wave a ninth block.  The unfused baseline uses the same plan.
+        rplan = {"split_factor": 2}
+        rkw = dict(rplan) if args.fused_merge is None else dict(rplan, fused_merge=args.fused_merge)
         runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, **rkw)
         m = timed(runner, args.steps, args.warmup)
         secondary["streaming_rope_decode"] = {
@@ -574,7 +578,7 @@ def main():
         rprob = runner.attn[0].problem
         t_rot = tensors_for(rprob, d0["q"], d0["k"], d0["v"], runner.out, runner.lse, page_indices=d0["pages"],
                             rope=runner.rope)
-        plain = make_attention(b, bsk.TILE_DECODE, 0, device, rope_mode=bsk.ROPE_NONE)
+        plain = make_attention(b, bsk.TILE_DECODE, 0, device, rope_mode=bsk.ROPE_NONE, **rplan)
         t_plain = tensors_for(plain.problem, q_out, k_out, d0["v"], runner.out, runner.lse, page_indices=d0["pages"])
         stream = torch.cuda.current_stream()
         plain.plan(b.qo_indptr, b.kv_len, runner.kv_indptr, stream=stream)
