@@ -74,11 +74,13 @@ def test_tiny_decode_f32_nhd_layout():
     compare(b, O, L, o_tol=1e-5, lse_tol=1e-5)
 
 
-def test_llama3_decode_full():
-    """64 requests, kv lognormal [512, 8192], 32/8 heads, d 128, bf16, page 16: the benchmarked launch."""
+@pytest.mark.parametrize("split", [1, 2])
+def test_llama3_decode_full(split):
+    """64 requests, kv lognormal [512, 8192], 32/8 heads, d 128, bf16, page 16: the benchmarked launch
+    (split factor 1, the decode default) and the finer split with more merged units."""
     b = W.llama3_decode()
-    say(f"llama3 decode: {int(b.kv_len.sum())} keys")
-    O, L, attn, _ = run(b)
+    say(f"llama3 decode: {int(b.kv_len.sum())} keys, split factor {split}")
+    O, L, attn, _ = run(b, split_factor=split)
     say(f"  plan: W={attn.info.num_workers} items={attn.info.num_items} chunk={attn.info.chunk} "
         f"merges={attn.info.num_merge}")
     compare(b, O, L)
@@ -310,11 +312,13 @@ def test_composable_concurrent_matches_sequential():
 
 # ------------------------------------------------------------------ fused RoPE + window + sinks
 
-def test_streaming_rope_full():
-    """batch 8, kv uniform [32768, 131072], 64/8 heads, window 4096 + 4 sinks, RoPE theta 5e5."""
+@pytest.mark.parametrize("split", [1, 2])
+def test_streaming_rope_full(split):
+    """batch 8, kv uniform [32768, 131072], 64/8 heads, window 4096 + 4 sinks, RoPE theta 5e5; split
+    factor 2 is the benchmarked launch (512-key chunks), 1 the decode default (528-key chunks)."""
     b = W.streaming_rope_decode()
-    say(f"streaming rope: kv {b.kv_len.tolist()}")
-    O, L, _, _ = run(b)
+    say(f"streaming rope: kv {b.kv_len.tolist()}, split factor {split}")
+    O, L, _, _ = run(b, split_factor=split)
     compare(b, O, L)
 
 
