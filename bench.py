@@ -7,13 +7,17 @@ Headline: paged GQA decode of a Llama-3-8B-shaped layer (batch 64, 32 q / 8
 kv heads, head_dim 128, bf16, page 16, kv lengths lognormal in [512, 8192]).
 One step = host plan + plan upload + decode kernel + state merge, i.e. the
 whole hot path for one batch; two workspaces alternate so the host plan of
-step i+1 and its upload (on a copy stream) overlap the GPU work of step i.  The KV cache is rotated over
-four device copies so no step reads what the previous one left in the
-256 MB Infinity Cache.  ``value`` is algorithmic bytes (visible K/V + q +
-out + lse + page ids) per wall-clock step, in TB/s.
+step i+1 and its upload (on a copy stream) overlap the GPU work of step i
+(--graph 1 replays each step's run + merge from a graph captured at set-up
+instead of launching them).  The KV cache is rotated over four
+device copies so no step reads what the previous one left in the 256 MB
+Infinity Cache.  ``value`` is algorithmic bytes (visible K/V + q + out +
+lse + page ids) per wall-clock step, in TB/s; the timed loop holds the
+steps only (no timing events, the garbage collector paused).
 
 Also reported (same JSON line): the decode kernel's roofline (HIP events on
-its own stream), the fp64 oracle timed on a bounded sample of the same
+its own stream, in a separate pass after the timed loop), the fp64 oracle
+timed on a bounded sample of the same
 batch on the host cores, and secondary measurements of the ragged causal
 prefill (TFLOP/s vs bf16 MFMA peak), the shared-prefix composable format,
 the fused-RoPE streaming decode and a mixed decode + prefill batch in one
@@ -93,12 +97,12 @@ def make_attention(batch, tile_q, out_dtype, device, **kw):
 class Runner:
     """Device copies of one batch plus two alternating plan workspaces."""
 
-    def __init__(self, batch, tile_q, copies, device, out_dtype=0, **plan_kw):
+    def __init__(self, batch, tile_q, copies, device, out_dtype=0, graphs=False, **plan_kw):
         import torch
 
         import block_sparse_kv_plan_amd as bsk
         from block_sparse_kv_plan_amd.attention import tensors_for
-        from tests.gpu_util import rope_positions_needed, upload
+        from workloads.device import rope_positions_needed, upload
         self.batch = batch
         self.attn = [make_attention(batch, tile_q, out_dtype, device, **plan_kw) for _ in range(2)]
         T = int(batch.qo_indptr[-1])
@@ -121,55 +125,87 @@ class Runner:
             self.dev.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in first.items()})
         self.tensors = [tensors_for(self.attn[0].problem, d["q"], d["k"], d["v"], o, l,
                                     page_indices=d["pages"], rope=self.rope) for d, (o, l) in zip(self.dev, self.outs)]
+        # run + merge of every (workspace, KV copy) pair a step uses, captured once (each workspace
+        # needs a plan before its launches can be recorded; later plans reuse the captures)
+        self.graphs = None
+        if graphs:
+            stream = torch.cuda.current_stream()
+            for a in self.attn:
+                a.plan(batch.qo_indptr, batch.kv_len, self.kv_indptr, stream=stream)
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            self.graphs = {(w, c): self.attn[w].capture(self.tensors[c], side)
+                           for w in range(2) for c in range(copies) if (w - c) % math.gcd(2, copies) == 0}
+            torch.cuda.synchronize()
 
-    def step(self, i, stream, ev=None, copy_stream=None):
-        """One pass of the hot path: host plan + upload (on the copy stream when given),
-        the attention kernel, then the split-KV state merge."""
+    def step(self, i, stream, copy_stream=None):
+        """One pass of the hot path: host plan + upload (on the copy stream when given), the
+        attention kernel, then the split-KV state merge (replayed from a graph when captured)."""
         a = self.attn[i % 2]
         a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, copy_stream=copy_stream)
-        t = self.tensors[i % len(self.tensors)]
-        if copy_stream is not None:
-            stream.wait_event(a._uploaded)  # before the kernel's start event, so that it times the kernel only
-        if ev is not None:
-            ev[0].record(stream)
-        a.run(t, stream=stream, merge=False, wait_upload=copy_stream is None)
-        if ev is not None:
-            ev[1].record(stream)
-        a.merge(t, stream)
-        if ev is not None:
-            ev[2].record(stream)
+        c = i % len(self.tensors)
+        if self.graphs is not None:
+            a.replay(self.graphs[(i % 2, c)], stream)
+        else:
+            a.run(self.tensors[c], stream=stream)
 
 
-def timed(runner, steps, warmup):
-    """Wall time per step over `steps` back-to-back steps, and the attention kernel's and the
-    merge's mean durations from events on their launch stream.  Plans are uploaded on a copy
-    stream (off the kernels' queue; a third stream for the merges measured slower); the
-    kernel / merge events are recorded on every eighth timed step (every fourth below 160 steps,
-    every step below 80), since each event is a packet on the kernels' queue and costs about
-    3 microseconds of its own."""
+def wall_clock(runner, steps, warmup):
+    """Wall time per step over `steps` back-to-back steps after `warmup` untimed ones.
+
+    Plans are uploaded on a copy stream (off the kernels' queue).  Nothing but the steps runs in
+    the timed loop: no timing events (kernel durations come from a separate pass,
+    kernel_durations()), and the Python garbage collector is paused, so the loop's contents do
+    not depend on `steps`.  Host stamps after each step's submission show whether the host kept
+    ahead of the GPU."""
+    import gc
+
+    import numpy as np
     import torch
     stream = torch.cuda.current_stream()
     copy_stream = torch.cuda.Stream()
-    every = 8 if steps >= 160 else (4 if steps >= 80 else 1)
     for i in range(warmup):
         runner.step(i, stream, copy_stream=copy_stream)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] if i % every == 0 else None for i in range(steps)]
-    for e in (x for trio in evs if trio is not None for x in trio):
-        e.record(stream)  # torch creates the HIP event at its first record: do that outside the timed region
+    stamps = np.zeros(steps)
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            runner.step(warmup + i, stream, copy_stream=copy_stream)
+            stamps[i] = time.perf_counter()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        gc.enable()
+    host = np.diff(np.concatenate([[t0], stamps])) * 1e6
+    return {"wall_s": (t1 - t0) / steps, "host_submit_us_median": round(float(np.median(host)), 1),
+            "host_submit_us_max": round(float(host.max()), 1), "drain_us": round((t1 - stamps[-1]) * 1e6, 1)}
+
+
+def kernel_durations(runner, reps):
+    """The attention kernel's launch duration from HIP events recorded on its own stream right
+    around it, over `reps` launches on the last plans (KV copies rotating as in the timed loop).
+    Runs after the wall-clock loop, so its events never share a queue with it."""
+    import torch
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        runner.step(warmup + i, stream, evs[i], copy_stream=copy_stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(3):
+        runner.attn[i % 2].run(runner.tensors[i % len(runner.tensors)], stream=stream)
+    for i, (e0, e1) in enumerate(evs):
+        a = runner.attn[i % 2]
+        t = runner.tensors[i % len(runner.tensors)]
+        e0.record(stream)
+        a.run(t, stream=stream, merge=False, wait_upload=False)
+        e1.record(stream)
+        a.merge(t, stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    kern = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs if e is not None]
-    merge = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs if e is not None]
-    kern.sort()
-    pct = lambda q: kern[min(len(kern) - 1, int(q * len(kern)))]
-    return {"wall_s": wall, "kernel_s_mean": sum(kern) / len(kern), "kernel_s_median": pct(0.5),
-            "kernel_s_p10": pct(0.1), "kernel_s_p90": pct(0.9), "kernel_s_min": kern[0],
-            "merge_s_mean": sum(merge) / len(merge), "event_samples": len(kern)}
+    k = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+    pct = lambda q: k[min(len(k) - 1, int(q * len(k)))]
+    return {"kernel_s_mean": sum(k) / len(k), "kernel_s_median": pct(0.5), "kernel_s_p10": pct(0.1),
+            "kernel_s_p90": pct(0.9), "kernel_s_min": k[0], "samples": len(k)}
 
 
 def plan_host_us(runner, calls=50):
@@ -199,8 +235,9 @@ def cpu_baseline(batch, budget_s=15.0):
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from tests.helpers import oracle_kv
-    kv = oracle_kv(batch)  # host view of the cache, built once outside the timed calls
+    from oracle.attention import PagedKV
+    kp, vp, idx = batch.host_pools()  # host view of the cache, built once outside the timed calls
+    kv = PagedKV(kp, vp, batch.kv_page_indptr, idx, batch.page_size)
     done, t_used, bytes_done = 0, 0.0, 0
     limits = threadpool_limits(limits=1)  # the oracle's one BLAS product runs single-threaded too
     for r in range(batch.batch_size):
@@ -298,7 +335,7 @@ def mixed_leg(device, reps):
     import block_sparse_kv_plan_amd as bsk
     import workloads as W
     from block_sparse_kv_plan_amd.attention import tensors_for
-    from tests.gpu_util import upload
+    from workloads.device import upload
     b = W.mixed()
     dec = b.qo_len == 1
     parts = {"mixed": (b, dict(tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE))}
@@ -369,6 +406,9 @@ def main():
     ap.add_argument("--fused-merge", type=int, choices=(0, 1), default=None,
                     help="merge split units in-kernel (1) or with the separate merge kernel (0) on the decode-class "
                          "workloads (Llama-3 decode, streaming RoPE decode)")
+    ap.add_argument("--graph", type=int, choices=(0, 1), default=0,
+                    help="replay each step's run + merge from a graph captured at set-up (1) or launch them "
+                         "directly (0, default: two direct launches measured faster than one graph launch)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
@@ -407,9 +447,10 @@ def main():
         dkw = {k: v for k, v in (("split_factor", args.decode_split), ("min_chunk", args.decode_min_chunk),
                                   ("item_overhead", args.decode_overhead), ("fused_merge", args.fused_merge))
                if v is not None}
-        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device, **dkw)
+        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device, graphs=bool(args.graph), **dkw)
         log(f"decode: {int(b.kv_len.sum())} keys, {nbytes / 1e9:.3f} GB per step; timing {args.steps} steps")
-        m = timed(runner, args.steps, args.warmup)
+        m = wall_clock(runner, args.steps, args.warmup)
+        m.update(kernel_durations(runner, max(20, min(args.steps, 100))))
         info = runner.attn[0].info
         achieved = nbytes / m["kernel_s_mean"] / 1e9
         plan_us = plan_host_us(runner)
@@ -433,8 +474,13 @@ def main():
                        "out_dtype": "f32", "num_workers": info.num_workers, "items": info.num_items,
                        "chunk": info.chunk, "merges": info.num_merge,
                        "plan_imbalance": round(info.max_load / max(1.0, info.total_cost / info.num_workers), 3),
-                       "plan_host_us": plan_us,
+                       "plan_host_us": plan_us, "graph_replay": bool(args.graph),
                        "parallelism": "single GPU"},
+            "timing": {"protocol": "wall clock over the timed steps (plan + upload on a copy stream + run + merge, "
+                                   "no events in the loop, garbage collector paused); kernel durations from HIP "
+                                   "events around the kernel in a separate pass afterwards",
+                       "host_submit_us_median": m["host_submit_us_median"],
+                       "host_submit_us_max": m["host_submit_us_max"], "drain_us": m["drain_us"]},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "kernel": "decode_kernel<bf16,128,paged>",
@@ -442,8 +488,7 @@ def main():
                          "kernel_us_median": round(m["kernel_s_median"] * 1e6, 2),
                          "kernel_us_p10": round(m["kernel_s_p10"] * 1e6, 2),
                          "kernel_us_p90": round(m["kernel_s_p90"] * 1e6, 2),
-                         "event_samples": m["event_samples"],
-                         "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
+                         "event_samples": m["samples"],
                          "algorithmic_bytes_per_launch": nbytes},
         }
         if not args.no_cpu:
@@ -457,7 +502,8 @@ def main():
         b = W.ragged_prefill()
         flops, pairs = prefill_flops(b)
         runner = Runner(b, prefill_tile, copies=1, device=device)
-        m = timed(runner, max(5, args.steps // 5), 3)
+        m = wall_clock(runner, max(5, args.steps // 10), 3)
+        m.update(kernel_durations(runner, max(10, min(args.steps // 5, 40))))
         tf = flops / m["kernel_s_mean"] / 1e12
         secondary["ragged_prefill"] = {
             "workload": "ragged_causal_prefill_append_bf16: 16 requests, q lognormal [128,4096] after "
@@ -472,7 +518,7 @@ def main():
     if not args.no_secondary and args.only in ("", "append"):
         log("append: new tokens' K/V of the ragged prefill into the paged cache; chunked prefill")
         from block_sparse_kv_plan_amd.attention import BatchAttention, chunked_prefill, pool_strides
-        from tests.gpu_util import upload
+        from workloads.device import upload
         b = W.ragged_prefill()
         du = upload(b, device=device)
         new = b.qo_len.astype(np.int64)
@@ -539,7 +585,7 @@ def main():
             us = []
             for ind in (0, 1):
                 runner = Runner(b, tq, copies=copies, device=device, independent_kv_strides=ind)
-                m = timed(runner, max(10, args.steps // 2) if name == "decode" else 8, 3)
+                m = kernel_durations(runner, max(20, min(args.steps, 100)) if name == "decode" else 10)
                 us.append(m["kernel_s_mean"] * 1e6)
                 del runner
                 torch.cuda.empty_cache()
@@ -558,15 +604,16 @@ def main():
         # default's 528-key chunks give one wave a ninth block.  The unfused baseline uses the same plan.
         rplan = {"split_factor": 2}
         rkw = dict(rplan) if args.fused_merge is None else dict(rplan, fused_merge=args.fused_merge)
-        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, **rkw)
-        m = timed(runner, args.steps, args.warmup)
+        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, graphs=bool(args.graph), **rkw)
+        m = wall_clock(runner, args.steps, args.warmup)
+        m.update(kernel_durations(runner, max(20, min(args.steps, 100))))
         secondary["streaming_rope_decode"] = {
             "workload": "streaming_rope_window_sink_decode_bf16: batch 8, kv uniform [32768,131072], 64q/8kv, "
                         "d128, window 4096 + 4 sinks, RoPE theta 5e5 in-kernel",
             "kernel_gbs": round(nbytes / m["kernel_s_mean"] / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / m["kernel_s_mean"] / 1e9 / HBM_PEAK_GBS, 4),
-            "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2), "merge_us_mean": round(m["merge_s_mean"] * 1e6, 2),
-            "step_us": round(m["wall_s"] * 1e6, 1), "algorithmic_bytes": nbytes}
+            "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2), "step_us": round(m["wall_s"] * 1e6, 1),
+            "algorithmic_bytes": nbytes}
         # unfused reference point: rotate the visible keys and the query into scratch, then a plain
         # windowed decode over (rotated K, V); same bytes credited as the fused kernel's
         from block_sparse_kv_plan_amd.attention import tensors_for

@@ -88,9 +88,9 @@ class BatchAttention:
     """Owns the workspaces of one problem; plan() per step, run() per layer.
 
     The plan upload can go on its own copy stream, and the merge can run on a stream of its own
-    (merge()): an upload waits (on the GPU) for the last run and the last merge that read this
-    workspace on other streams, and run() waits for the upload, so a host plan, its copy and the
-    previous step's merge overlap the GPU work already queued."""
+    (merge()): plan() first waits (on the host) for the last run and the last merge that read this
+    workspace on other streams, and run() waits (on the GPU) for the upload, so a host plan, its
+    copy and the previous step's merge overlap the GPU work already queued."""
 
     def __init__(self, problem: Problem, device="cuda"):
         self.problem = problem
@@ -121,8 +121,12 @@ class BatchAttention:
         stream = stream or torch.cuda.current_stream(self.device)
         up = copy_stream if copy_stream is not None else stream
         self._settle_run()
-        # do not overwrite int_ws under a kernel that still reads it on another stream: wait for the
-        # last run and the last merge (one wait when both went to the same stream, the merge last)
+        # Do not overwrite int_ws under a kernel that still reads it on another stream: wait for the
+        # last run and the last merge (one wait when both went to the same stream, the merge last).
+        # The wait is on the host.  A GPU-side wait queued in front of the upload made every copy
+        # behind it cost ~50 us of host time in the runtime, and once per process stalled one copy
+        # for several milliseconds; with two or more workspaces in turn the last run on this one
+        # has normally finished by the time it is planned again, so the host wait returns at once.
         waits = []
         if self._merged_stream is not None:
             waits.append((self._merged, self._merged_stream))
@@ -130,7 +134,7 @@ class BatchAttention:
             waits.append((self._consumed, self._consumed_stream))
         for ev, st in waits:
             if st != up:
-                up.wait_event(ev)
+                ev.synchronize()
         self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
                          self.host_ws, self.int_ws, up)
         self._uploaded.record(up)
@@ -165,6 +169,38 @@ class BatchAttention:
             self._consumed.record(self._run_stream)
             self._consumed_stream = self._run_stream
             self._run_stream = None
+
+    def capture(self, tensors: Tensors, stream=None) -> "torch.cuda.CUDAGraph":
+        """Record this workspace's run (and merge, unless it is fused) for `tensors` in a graph.
+
+        The run and merge launches read every per-step value from the int workspace (FlashInfer
+        paper summary, "Research methodology" 3: a plan cached on the GPU drives a fixed launch),
+        so one capture serves every later plan into the same workspace; replay() runs it after
+        each plan().  `stream` is the capturing stream (a side stream is made if none is given)."""
+        stream = stream or torch.cuda.Stream(self.device)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            if self.problem.tile_q == TILE_DECODE:
+                run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+            else:
+                run_prefill(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+            if not self.problem.fused_merge:
+                merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        return graph
+
+    def replay(self, graph: "torch.cuda.CUDAGraph", stream=None):
+        """Run a graph from capture() on `stream` for the last plan: waits for the plan's upload
+        when it went to another stream, and counts as the run and merge of this workspace for the
+        next plan's reuse checks."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        if self._upload_stream is not None and self._upload_stream != stream:
+            stream.wait_event(self._uploaded)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        self._merged.record(stream)
+        self._merged_stream = stream
+        self._consumed_stream = None
+        self._run_stream = None
 
     def merge(self, tensors: Tensors, stream=None):
         """The split-KV merge of the last run (nothing when the run merged in-kernel).  On another
@@ -243,18 +279,23 @@ def chunked_prefill(attn: BatchAttention, q, k_new, v_new, out, lse, k_pool, v_p
     starts = np.concatenate([[0], np.cumsum(new_len)])
     n_total = int(starts[-1])
     page_indptr_host = np.asarray(kv_page_indptr, dtype=np.int32)
-    page_indptr_dev = torch.as_tensor(page_indptr_host).to(attn.device)
     ks, vs = pool_strides(k_pool, layout), pool_strides(v_pool, layout)
     p = attn.problem
+    # The device index arrays are allocated while `stream` is current: the caching allocator then
+    # hands their blocks only to later allocations on `stream`, which run after the appends that
+    # read them, so a caller's stream other than the current one is safe.
+    steps = []
     for c0 in range(0, n_total, chunk_tokens):
         c1 = min(c0 + chunk_tokens, n_total)
         lo = np.clip(c0 - starts[:-1], 0, new_len)
         hi = np.clip(c1 - starts[:-1], 0, new_len)
-        cnt = hi - lo
-        qo_indptr = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+        qo_indptr = np.concatenate([[0], np.cumsum(hi - lo)]).astype(np.int32)
         kv_len = (prefix_len + hi).astype(np.int32)
-        app_dev = torch.as_tensor(qo_indptr).to(attn.device, non_blocking=False)
-        kvl_dev = torch.as_tensor(kv_len).to(attn.device, non_blocking=False)
+        steps.append((c0, c1, qo_indptr, kv_len))
+    with torch.cuda.stream(stream):
+        page_indptr_dev = torch.as_tensor(page_indptr_host).to(attn.device)
+        dev = [(torch.as_tensor(qo).to(attn.device), torch.as_tensor(kl).to(attn.device)) for _, _, qo, kl in steps]
+    for (c0, c1, qo_indptr, kv_len), (app_dev, kvl_dev) in zip(steps, dev):
         kn, vn = k_new[c0:c1], v_new[c0:c1]
         append_paged_kv(p, len(new_len), c1 - c0, app_dev, kvl_dev, page_indptr_dev, page_indices, kn, vn,
                         kn.stride(0), kn.stride(1), k_pool, v_pool, ks, vs, stream)

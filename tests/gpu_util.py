@@ -10,6 +10,7 @@ import torch
 import block_sparse_kv_plan_amd as bsk
 from block_sparse_kv_plan_amd.attention import BatchAttention, make_problem, tensors_for
 from tests.helpers import oracle_attention
+from workloads.device import rope_positions_needed, torch_dtype, upload  # noqa: F401 (re-exported)
 
 O_TOL = 1e-2    # max-abs on O: bf16 inputs, fp32 accumulation
 LSE_TOL = 1e-3  # max-abs on LSE
@@ -26,40 +27,7 @@ def require_gpu():
 
 
 def tdtype(batch):
-    return torch.bfloat16 if batch.dtype == "bf16" else torch.float32
-
-
-def upload(batch, layout="HND", device="cuda:0"):
-    """Device tensors for a batch: q, the physical K/V pool (NaN where no live page),
-    page table and lengths."""
-    dt = tdtype(batch)
-    dev = torch.device(device)
-    out = {"q": torch.from_numpy(batch.q).to(dt).to(dev)}
-    if batch.kv_mode == "dense":
-        out["k"] = torch.from_numpy(batch.dense_k).to(dt).to(dev)
-        out["v"] = torch.from_numpy(batch.dense_v).to(dt).to(dev)
-        out["kv_indptr"] = batch.kv_indptr.astype(np.int32)
-        out["pages"] = None
-        return out
-    shape = (batch.num_pages, batch.num_kv_heads, batch.page_size, batch.head_dim)
-    k = torch.full(shape, float("nan"), dtype=dt, device=dev)
-    v = torch.full(shape, float("nan"), dtype=dt, device=dev)
-    phys = torch.from_numpy(batch.kv_page_indices[batch.live_logical].astype(np.int64)).to(dev)
-    k[phys] = torch.from_numpy(batch.k_live).to(dt).to(dev)
-    v[phys] = torch.from_numpy(batch.v_live).to(dt).to(dev)
-    if layout == "NHD":
-        k = k.transpose(1, 2).contiguous()
-        v = v.transpose(1, 2).contiguous()
-    out["k"], out["v"] = k, v
-    out["pages"] = torch.from_numpy(batch.kv_page_indices.astype(np.int32)).to(dev)
-    out["kv_indptr"] = batch.kv_page_indptr.astype(np.int32)
-    return out
-
-
-def rope_positions_needed(batch):
-    if batch.rope == "streaming" and batch.window > 0:
-        return int(min(int(batch.kv_len.max()), batch.window + batch.sink))
-    return int(batch.kv_len.max())
+    return torch_dtype(batch)
 
 
 def run(batch, tile_q=bsk.TILE_DECODE, out_dtype=bsk.DTYPE_F32, layout="HND", dev_tensors=None, num_workers=None,

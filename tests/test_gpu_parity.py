@@ -421,6 +421,47 @@ def test_graph_capture_replan_replay():
         _ = (out * 2).sum().item()  # eager work between replays
 
 
+def test_capture_replay_alternating_workspaces():
+    """BatchAttention.capture / replay as the benchmark uses them: two workspaces, a graph per
+    (workspace, output) pair captured once, a new plan (other lengths) uploaded on a copy stream
+    before every replay.  Every replay equals the eager run + merge of the same plan bit for bit,
+    and the oracle; eager work and synchronisations run between the replays."""
+    dev = require_gpu()
+    lens = [[900, 2000, 33, 512], [17, 1500, 33, 2], [640, 640, 640, 640], [4000, 1, 77, 1999]]
+    b = small(81, [4000, 2000, 640, 1999], Hq=32, Hk=8, d=128, causal=True)
+    du = upload(b)
+    attn = [BatchAttention.create(device=dev, num_qo_heads=32, num_kv_heads=8, head_dim=128, dtype=bsk.DTYPE_BF16,
+                                  causal=True, max_batch=4, split_factor=3, min_chunk=64) for _ in range(2)]
+    outs = [(torch.zeros((4, 32, 128), dtype=torch.float32, device=dev), torch.zeros((4, 32), device=dev))
+            for _ in range(2)]
+    ts = [tensors_for(attn[0].problem, du["q"], du["k"], du["v"], o, l, page_indices=du["pages"]) for o, l in outs]
+    main = torch.cuda.current_stream()
+    for a in attn:
+        a.plan(b.qo_indptr, b.kv_len, du["kv_indptr"], stream=main)
+    torch.cuda.synchronize()
+    graphs = [attn[w].capture(ts[w]) for w in range(2)]
+    copy = torch.cuda.Stream()
+    for step in range(8):
+        w = step % 2
+        kv = np.minimum(np.asarray(lens[step % 4]), b.kv_len)
+        say(f"replay step {step}: workspace {w}, kv {kv.tolist()}")
+        info = attn[w].plan(b.qo_indptr, kv, du["kv_indptr"], stream=main, copy_stream=copy)
+        outs[w][0].fill_(float("nan"))
+        attn[w].replay(graphs[w], main)
+        torch.cuda.synchronize()
+        got = (outs[w][0].clone(), outs[w][1].clone())
+        outs[w][0].fill_(float("nan"))
+        attn[w].run(ts[w], stream=main)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], outs[w][0]) and torch.equal(got[1], outs[w][1]), f"step {step}"
+        if step < 4:
+            assert info.num_merge > 0
+            bt = small(81, [4000, 2000, 640, 1999], Hq=32, Hk=8, d=128, causal=True)
+            bt.kv_len = kv.astype(np.int32)
+            compare(bt, got[0].double().cpu().numpy(), got[1].double().cpu().numpy())
+        _ = (outs[1 - w][0] * 2).sum().item()  # eager work between replays
+
+
 # ------------------------------------------------------------------ K/V stride specialisation
 
 @pytest.mark.parametrize("tile_q", [bsk.TILE_DECODE, bsk.TILE_PREFILL, bsk.TILE_PREFILL_256])
