@@ -71,7 +71,7 @@ _sig = {
     "bsk_plan": [P(Problem), i32, vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, P(PlanInfo)],
     "bsk_run_decode": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
     "bsk_run_prefill": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
-    "bsk_merge_states": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp],
+    "bsk_merge_states": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
     "bsk_merge_state_pair": [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp],
     "bsk_rope_table": [vp, i32, i32, f64, vp],
     "bsk_debug_gather": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp, vp, vp],
@@ -168,7 +168,7 @@ def run_prefill(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, floa
 
 def merge_states(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, float_ws, stream=None):
     _ok(_lib.bsk_merge_states(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
-                              _ptr(float_ws), _stream(stream)))
+                              _ptr(float_ws), 0 if float_ws is None else _nbytes(float_ws), _stream(stream)))
 
 
 def merge_state_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows: int, head_dim: int, out_dtype: int,

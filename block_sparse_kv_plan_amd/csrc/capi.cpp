@@ -118,15 +118,26 @@ size_t float_ws_need(const bsk_problem& p) {
   return size_t(p.max_slots) * size_t(p.tile_q) * size_t(p.head_dim + 1) * sizeof(float);
 }
 
+// The plan must have been built for this problem: the kernels take the slot stride and the launch
+// grid from the problem, the item and merge records from the plan.
+bsk_status check_plan_matches(const bsk_problem& p, const bsk_plan_info& info) {
+  if (info.tile_q != p.tile_q) return fail(BSK_ERR_INVALID_ARG, "plan was built for another query-tile class");
+  if (info.num_workers != p.num_workers) return fail(BSK_ERR_INVALID_ARG, "plan info does not match problem");
+  if (info.num_slots < 0 || info.num_slots > p.max_slots || info.num_merge < 0 || info.num_merge > p.max_merge)
+    return fail(BSK_ERR_INVALID_ARG, "plan slots / merge entries exceed the problem's capacities");
+  return BSK_OK;
+}
+
 bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_tensors* t, const void* int_ws,
                      void* float_ws, size_t float_ws_bytes, int tile_q) {
   bsk_status s = check_problem(p);
   if (s != BSK_OK) return s;
   if (!info || !t || !int_ws) return fail(BSK_ERR_INVALID_ARG, "plan info, tensors and int workspace are required");
   const bool want_prefill = tile_q != BSK_TILE_DECODE;
-  if ((want_prefill ? !is_prefill_tile(p->tile_q) : p->tile_q != tile_q) || info->tile_q != p->tile_q)
+  if (want_prefill ? !is_prefill_tile(p->tile_q) : p->tile_q != tile_q)
     return fail(BSK_ERR_INVALID_ARG, "plan was built for the other query-tile class");
-  if (info->num_workers != p->num_workers) return fail(BSK_ERR_INVALID_ARG, "plan info does not match problem");
+  s = check_plan_matches(*p, *info);
+  if (s != BSK_OK) return s;
   if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*p)))
     return fail(BSK_ERR_WORKSPACE, "float workspace smaller than bsk_workspace_query");
   const size_t ebytes = p->dtype == BSK_DTYPE_BF16 ? 2 : 4;
@@ -346,11 +357,14 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
 }
 
 bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
-                            const void* int_ws_dev, const void* float_ws, void* stream) {
+                            const void* int_ws_dev, const void* float_ws, size_t float_ws_bytes, void* stream) {
   bsk_status s = check_problem(problem);
   if (s != BSK_OK) return s;
   if (!info || !t || !int_ws_dev || !t->out || !t->lse) return fail(BSK_ERR_INVALID_ARG, "null argument");
-  if (info->num_slots > 0 && !float_ws) return fail(BSK_ERR_INVALID_ARG, "float workspace is NULL");
+  s = check_plan_matches(*problem, *info);
+  if (s != BSK_OK) return s;
+  if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*problem)))
+    return fail(BSK_ERR_WORKSPACE, "float workspace missing or smaller than bsk_workspace_query");
   if (!aligned(t->out, problem->out_dtype == BSK_DTYPE_F32 ? 16 : 8) || t->o_stride_tok % 4 || t->o_stride_head % 4)
     return fail(BSK_ERR_INVALID_ARG, "out must be aligned to 4 elements (strides too)");
   bsk::MergeArgs a;

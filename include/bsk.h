@@ -260,18 +260,26 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
  * O = sum_c exp(LSE_c - LSE) * O_c, written to t->out / t->lse.  Rows of
  * single-chunk units are left untouched (already written by run).  Needed
  * after a run with problem.fused_merge = 0; after a fused run it recomputes
- * the same values.  Fixed grid.  Errors: INVALID_ARG, HIP.
+ * the same values.  float_ws / float_ws_bytes: the workspace the run wrote
+ * its partial states to (at least the float size bsk_workspace_query gives
+ * for `problem`).  Fixed grid.  Checked on the host before anything is
+ * enqueued: the plan must belong to `problem` (same query-tile class and
+ * worker count, slots and merge entries within its capacities).
+ * Errors: INVALID_ARG (null pointers, plan / problem mismatch, misaligned
+ * out), WORKSPACE (float workspace missing or smaller than required), HIP.
  */
 bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
-                            const void* int_ws_dev, const void* float_ws, void* stream);
+                            const void* int_ws_dev, const void* float_ws, size_t float_ws_bytes, void* stream);
 
 /*
  * Merge two complete states row by row (the composable format's dense
  * prefix state with a sparse suffix state, [FI-paper, methodology 1]):
  * o_a/o_b [rows, head_dim] f32 contiguous, lse_a/lse_b [rows] f32; writes
- * o_out [rows, head_dim] in out_dtype and lse_out [rows].  Rows whose two
- * LSEs are both -inf get O = 0, LSE = -inf.  o_out may alias o_a or o_b
- * only when out_dtype is F32.  Errors: INVALID_ARG, HIP.
+ * o_out [rows, head_dim] in out_dtype and lse_out [rows].  A row is one
+ * (query token, q head) pair: for attention outputs laid out [T, Hq, d]
+ * with contiguous heads, rows = T * Hq.  Rows whose two LSEs are both
+ * -inf get O = 0, LSE = -inf.  o_out may alias o_a or o_b only when
+ * out_dtype is F32.  Errors: INVALID_ARG, HIP.
  */
 bsk_status bsk_merge_state_pair(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
                                 void* o_out, float* lse_out, int32_t rows, int32_t head_dim, int32_t out_dtype,

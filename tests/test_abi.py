@@ -67,3 +67,75 @@ int main(void) {
             s, m = key.split(".")
             cls = {"bsk_problem": bsk.Problem, "bsk_plan_info": bsk.PlanInfo, "bsk_tensors": bsk.Tensors}[s]
             assert getattr(cls, m).offset == int(val), key
+
+
+def _planned_problem():
+    """A decode problem and a host-only plan of it with split units (partial-state slots > 0)."""
+    import numpy as np
+    from block_sparse_kv_plan_amd.attention import make_problem
+    p = make_problem(num_qo_heads=8, num_kv_heads=2, head_dim=128, dtype=bsk.DTYPE_BF16, causal=True, num_workers=4,
+                     split_factor=4, min_chunk=64, max_batch=4)
+    _, float_b, host_b = bsk.workspace_query(p)
+    kv = np.array([900, 300, 77], dtype=np.int32)
+    qo = np.array([0, 1, 2, 3], dtype=np.int32)
+    ki = np.concatenate([[0], np.cumsum((kv + 15) // 16)]).astype(np.int32)
+    info = bsk.plan(p, qo, kv, ki, np.zeros(host_b, dtype=np.uint8))
+    assert info.num_slots > 0 and info.num_merge > 0
+    t = bsk.Tensors()
+    t.q = t.k = t.v = t.out = t.lse = t.kv_page_indices = 0x10000  # never dereferenced: checks come first
+    t.q_stride_tok, t.q_stride_head, t.o_stride_tok, t.o_stride_head, t.lse_stride_tok = 8 * 128, 128, 8 * 128, 128, 8
+    t.k_stride_page = t.v_stride_page = 2 * 16 * 128
+    t.k_stride_head = t.v_stride_head = 16 * 128
+    t.k_stride_tok = t.v_stride_tok = 128
+    return p, info, t, float_b
+
+
+def _clone(x):
+    return type(x).from_buffer_copy(x)
+
+
+def _merge_status(p, info, t, int_ws, float_ws, float_bytes):
+    import ctypes as C
+    return bsk._lib.bsk_merge_states(C.byref(p), C.byref(info), C.byref(t), int_ws, float_ws, float_bytes, None)
+
+
+def test_merge_states_rejects_bad_workspaces_and_mismatched_plans():
+    """bsk_merge_states checks on the host, before anything is enqueued, what the run calls check:
+    the float workspace against bsk_workspace_query and the plan against the problem."""
+    p, info, t, float_b = _planned_problem()
+    fake = 0x20000
+    assert _merge_status(p, info, t, fake, None, 0) == bsk.ERR_WORKSPACE
+    assert "float workspace" in bsk.last_error()
+    assert _merge_status(p, info, t, fake, fake, float_b - 4) == bsk.ERR_WORKSPACE
+    bad = _clone(info)
+    bad.tile_q = bsk.TILE_PREFILL
+    assert _merge_status(p, bad, t, fake, fake, float_b) == bsk.ERR_INVALID_ARG
+    assert "query-tile class" in bsk.last_error()
+    bad = _clone(info)
+    bad.num_workers = info.num_workers + 1
+    assert _merge_status(p, bad, t, fake, fake, float_b) == bsk.ERR_INVALID_ARG
+    bad = _clone(info)
+    bad.num_slots = p.max_slots + 1
+    assert _merge_status(p, bad, t, fake, fake, float_b) == bsk.ERR_INVALID_ARG
+    assert "capacities" in bsk.last_error()
+    bad = _clone(info)
+    bad.num_merge = p.max_merge + 1
+    assert _merge_status(p, bad, t, fake, fake, float_b) == bsk.ERR_INVALID_ARG
+    assert _merge_status(p, info, t, None, fake, float_b) == bsk.ERR_INVALID_ARG
+    t2 = _clone(t)
+    t2.out = 0x10004  # not 16-byte aligned for f32 out
+    assert _merge_status(p, info, t2, fake, fake, float_b) == bsk.ERR_INVALID_ARG
+
+
+def test_run_rejects_the_same_inputs():
+    import ctypes as C
+    p, info, t, float_b = _planned_problem()
+    fake = 0x20000
+    run = lambda i, fw, fb: bsk._lib.bsk_run_decode(C.byref(p), C.byref(i), C.byref(t), fake, fw, fb, None)
+    assert run(info, fake, float_b - 4) == bsk.ERR_WORKSPACE
+    bad = _clone(info)
+    bad.num_slots = p.max_slots + 1
+    assert run(bad, fake, float_b) == bsk.ERR_INVALID_ARG
+    bad = _clone(info)
+    bad.num_workers = 3
+    assert run(bad, fake, float_b) == bsk.ERR_INVALID_ARG
