@@ -262,8 +262,8 @@ def cpu_baseline(batch, budget_s=15.0):
     except OSError:
         pass
     return {"value": bytes_done / t_used / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {batch.batch_size} requests of the same batch (fp64 numpy; einsum for the "
-                      f"logits, BLAS held to one thread for the P V product), {t_used:.1f} s",
+            "sample": f"{done} of {batch.batch_size} requests of the same batch (fp64 numpy, BLAS held to "
+                      f"one thread for its two matrix products), {t_used:.1f} s",
             "cpu": model, "cores_available": len(os.sched_getaffinity(0)), "blas_threads": 1}
 
 

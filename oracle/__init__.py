@@ -34,10 +34,12 @@ something other than itself (library routines, closed forms, invariants,
 brute force); see each docstring.
 """
 from .attention import (attention, attention_partial, gather_kv, merge, rope_rotate,
-                        visible, key_positions, composable, flat_from_composable)
+                        visible, key_positions, composable, flat_from_composable, round_to_bf16,
+                        attention_rope_stored)
 from .plan import plan_ref, PlanParams, PlanError
 from .append import append_paged_kv
 
 __all__ = ["attention", "attention_partial", "gather_kv", "merge", "rope_rotate", "visible",
-           "key_positions", "composable", "flat_from_composable", "plan_ref", "PlanParams", "PlanError",
+           "key_positions", "composable", "flat_from_composable", "round_to_bf16",
+           "attention_rope_stored", "plan_ref", "PlanParams", "PlanError",
            "append_paged_kv"]

@@ -123,6 +123,23 @@ def rope_rotate(x: np.ndarray, pos, theta: float) -> np.ndarray:
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Store real values in bfloat16, round to nearest, ties to even, returned as fp64.
+
+    bfloat16 keeps the sign, the 8 exponent bits and the top 7 fraction bits of an IEEE
+    binary32 number.  The value is rounded to binary32 first and then to bfloat16, the two
+    roundings a value computed in binary32 and stored as bfloat16 goes through: the low 16
+    bits of the binary32 pattern are rounded away by adding half of the dropped unit, minus
+    one unless the kept part is odd (ties to even), and clearing them.  Finite inputs whose
+    rounding stays finite only.  Pinned by: torch's own float32 -> bfloat16 conversion,
+    ties included (tests)."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    bits = x32.view(np.uint32).astype(np.uint64)
+    keep_odd = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + keep_odd) >> 16) << 16
+    return rounded.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def _softmax_rows(s: np.ndarray, allowed: np.ndarray, v: np.ndarray):
     """Masked softmax attention for logits s [..., n], mask [..., n], values v [n, d].
     Rows with nothing visible get O = 0, LSE = -inf."""
@@ -166,7 +183,9 @@ def _attend_request(q_r, qpos, kv, r, kv_len, h, g, sm_scale, causal, window, si
             pk = pk_all[np.searchsorted(vis_keys, J)]
             K = rope_rotate(K, pk, theta)
             qb = rope_rotate(qb, np.full(qb.shape[:-1], pq), theta)
-        s = sm_scale * np.einsum("agd,jd->agj", qb, K)
+        # all rows of the block against all gathered keys as one matrix product (a library
+        # primitive: the inner products of the definition, summed in BLAS order)
+        s = sm_scale * (qb.reshape(-1, d) @ K.T).reshape(qb.shape[:-1] + (len(J),))
         o, lse = _softmax_rows(s, use[:, None, J], V)
         O[a0:a1] = o
         L[a0:a1] = lse
@@ -207,6 +226,45 @@ def attention(q, qo_indptr, kv_len, kv, num_kv_heads, sm_scale, causal=False, wi
                                      causal, window, sink, rope, rope_theta)
             O[t0 + sel, heads, :] = o
             L[t0 + sel, heads] = lse
+    return O, L
+
+
+def attention_rope_stored(q, qo_indptr, kv_len, kv, num_kv_heads, sm_scale, window, sink, rope, rope_theta,
+                          store=round_to_bf16):
+    """RoPE attention as an unfused pipeline computes it: rotate, store, then plain attention.
+
+    Reading taken for the unfused reference point of the fused RoPE kernel [FI-paper, results:
+    fused RoPE + attention kernel]: a separate pass rotates every decode query (one per
+    request, its last token at qpos = kv_len - 1) and the keys that query sees (causal, window
+    plus sinks), at the positions ``key_positions`` gives, and writes them back in the cache's
+    element type; the attention pass then reads those stored values with no rotation of its
+    own.  Here the rotation is exact (``rope_rotate`` in fp64) and ``store`` is the storage
+    rounding (bf16 round to nearest even by default); the softmax is as in ``attention``.
+    Returns O [T, Hq, d] and LSE [T, Hq].  Pinned by: with ``store`` the identity it equals
+    ``attention(..., rope=mode)`` (tests)."""
+    q = np.asarray(q, dtype=np.float64)
+    T, Hq, d = q.shape
+    g = Hq // num_kv_heads
+    O = np.full((T, Hq, d), np.nan)
+    L = np.full((T, Hq), np.nan)
+    for r in range(len(kv_len)):
+        t0, t1 = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        if t1 == t0:
+            continue
+        assert t1 - t0 == 1, "the unfused reading rotates one decode query per request"
+        Lr = int(kv_len[r])
+        qpos = Lr - 1
+        vis = np.nonzero(visible(qpos, np.arange(Lr), Lr, True, window, sink))[0]
+        kpos, pq = key_positions(qpos, vis, rope)
+        K, V = gather_kv(kv, r, vis)                                   # [n, Hk, d]
+        Ks = store(rope_rotate(K, kpos[:, None], rope_theta))
+        qs = store(rope_rotate(q[t0], np.full(Hq, pq), rope_theta))    # [Hq, d]
+        for h in range(num_kv_heads):
+            heads = slice(h * g, (h + 1) * g)
+            s = sm_scale * (qs[heads] @ Ks[:, h, :].T)                 # [g, n]
+            o, lse = _softmax_rows(s, np.ones(s.shape, dtype=bool), V[:, h, :])
+            O[t0, heads] = o
+            L[t0, heads] = lse
     return O, L
 
 

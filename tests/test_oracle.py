@@ -312,6 +312,38 @@ def test_rope_streaming_positions_brute_force():
     assert pq == len(vis) - 1
 
 
+def test_round_to_bf16_matches_torch():
+    """The oracle's bf16 storage rounding equals torch's float32 -> bfloat16 conversion, on normal
+    draws, wide magnitudes, subnormals, signed zeros and exact ties (both parities)."""
+    import torch
+    rng = np.random.default_rng(29)
+    x = np.concatenate([rng.standard_normal(20000), rng.standard_normal(2000) * 1e30,
+                        rng.standard_normal(2000) * 1e-30, [0.0, -0.0, 1e-40, -3e-41]])
+    kept = rng.integers(0, 1 << 16, size=4000, dtype=np.uint64) << 16
+    ties = (kept | 0x8000) & 0x7F7FFFFF  # exactly half a bf16 unit below the next value
+    x = np.concatenate([x, ties.astype(np.uint32).view(np.float32).astype(np.float64)])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_to_bf16(x)
+    np.testing.assert_array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+@pytest.mark.parametrize("mode", ["streaming", "absolute"])
+def test_rope_stored_without_rounding_is_rope_attention(mode):
+    """The rotate-store-attend reading with the identity as storage equals the RoPE attention of
+    attention() (window, sinks, both position modes); bf16 storage moves it."""
+    b = small_paged(kv=(70, 9, 33, 120), qo=1, causal=True, window=24, sink=3, rope=mode, rope_theta=500000.0,
+                    seed=31, d=32, dtype=W.BF16)
+    O1, L1 = oracle_attention(b)
+    O2, L2 = oracle.attention_rope_stored(b.q, b.qo_indptr, b.kv_len, oracle_kv(b), b.num_kv_heads, b.sm_scale,
+                                          b.window, b.sink, mode, b.rope_theta, store=lambda x: x)
+    np.testing.assert_allclose(O2, O1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L2, L1, rtol=0, atol=1e-12)
+    O3, L3 = oracle.attention_rope_stored(b.q, b.qo_indptr, b.kv_len, oracle_kv(b), b.num_kv_heads, b.sm_scale,
+                                          b.window, b.sink, mode, b.rope_theta)
+    assert 1e-6 < np.abs(L3 - L1).max() < 1e-1
+
+
 # ---------------------------------------------------------------- plan
 
 def _params(**kw):
