@@ -27,6 +27,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20  # BSK_NOALLOC_SCRATCH_BYTES
 DTYPE_F32, DTYPE_BF16 = 0, 1
 KV_PAGED, KV_DENSE = 0, 1
 ROPE_NONE, ROPE_STREAMING, ROPE_ABSOLUTE = 0, 1, 2
@@ -73,6 +74,7 @@ _sig = {
     "bsk_run_prefill": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
     "bsk_merge_states": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
     "bsk_merge_state_pair": [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp],
+    "bsk_run_noalloc": [P(Problem), P(PlanInfo), P(Tensors), vp, vp],
     "bsk_rope_table": [vp, i32, i32, f64, vp],
     "bsk_debug_gather": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp, vp, vp],
     "bsk_rope_apply": [P(Problem), i32, i32, vp, vp, vp, P(Tensors), vp, i64, i64, vp, vp],
@@ -169,6 +171,11 @@ def run_prefill(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, floa
 def merge_states(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, float_ws, stream=None):
     _ok(_lib.bsk_merge_states(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
                               _ptr(float_ws), 0 if float_ws is None else _nbytes(float_ws), _stream(stream)))
+
+
+def run_noalloc(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, stream=None):
+    _ok(_lib.bsk_run_noalloc(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
+                             _stream(stream)))
 
 
 def merge_state_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows: int, head_dim: int, out_dtype: int,

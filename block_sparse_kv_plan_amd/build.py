@@ -27,7 +27,7 @@ ARCH = "gfx950"
 # packed-fp32 instructions are kept out of the device code on purpose
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops"]
-DEVICE_SOURCES = ["decode.hip", "prefill.hip", "mixed.hip", "merge.hip", "append.hip", "rope.hip"]
+DEVICE_SOURCES = ["decode.hip", "prefill.hip", "mixed.hip", "merge.hip", "append.hip", "rope.hip", "noalloc.hip"]
 # per-file extras: the prefill kernel's logits are never NaN when they reach fmaxf (masked ones are
 # -inf), so it is built without NaN semantics and its max needs no operand canonicalisation
 EXTRA = {"prefill.hip": ["-fno-honor-nans"], "mixed.hip": ["-fno-honor-nans"]}

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <string>
 
@@ -128,8 +129,9 @@ bsk_status check_plan_matches(const bsk_problem& p, const bsk_plan_info& info) {
   return BSK_OK;
 }
 
-bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_tensors* t, const void* int_ws,
-                     void* float_ws, size_t float_ws_bytes, int tile_q) {
+// Everything a run checks except the float workspace.
+bsk_status check_run_inputs(const bsk_problem* p, const bsk_plan_info* info, const bsk_tensors* t,
+                            const void* int_ws, int tile_q) {
   bsk_status s = check_problem(p);
   if (s != BSK_OK) return s;
   if (!info || !t || !int_ws) return fail(BSK_ERR_INVALID_ARG, "plan info, tensors and int workspace are required");
@@ -138,8 +140,6 @@ bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_
     return fail(BSK_ERR_INVALID_ARG, "plan was built for the other query-tile class");
   s = check_plan_matches(*p, *info);
   if (s != BSK_OK) return s;
-  if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*p)))
-    return fail(BSK_ERR_WORKSPACE, "float workspace smaller than bsk_workspace_query");
   const size_t ebytes = p->dtype == BSK_DTYPE_BF16 ? 2 : 4;
   const int64_t vec = 16 / int64_t(ebytes);
   if (!t->q || !t->k || !t->v || !t->out || !t->lse) return fail(BSK_ERR_INVALID_ARG, "null tensor");
@@ -164,7 +164,17 @@ bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_
   return BSK_OK;
 }
 
-bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* int_ws, void* float_ws) {
+bsk_status check_run(const bsk_problem* p, const bsk_plan_info* info, const bsk_tensors* t, const void* int_ws,
+                     void* float_ws, size_t float_ws_bytes, int tile_q) {
+  bsk_status s = check_run_inputs(p, info, t, int_ws, tile_q);
+  if (s != BSK_OK) return s;
+  if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*p)))
+    return fail(BSK_ERR_WORKSPACE, "float workspace smaller than bsk_workspace_query");
+  return BSK_OK;
+}
+
+bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* int_ws, float* part_o,
+                        float* part_lse) {
   bsk::AttnArgs a;
   a.q = t.q;
   a.q_st = t.q_stride_tok;
@@ -183,9 +193,8 @@ bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* 
   a.o_sh = t.o_stride_head;
   a.lse = t.lse;
   a.lse_st = t.lse_stride_tok;
-  float* fw = static_cast<float*>(float_ws);
-  a.part_o = fw;
-  a.part_lse = fw ? fw + size_t(p.max_slots) * p.tile_q * p.head_dim : nullptr;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
   a.ws = static_cast<const int32_t*>(int_ws);
   a.ws_rw = static_cast<int32_t*>(const_cast<void*>(int_ws));
   a.fused_merge = p.fused_merge != 0;
@@ -199,6 +208,80 @@ bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* 
   a.out_bf16 = p.out_dtype == BSK_DTYPE_BF16;
   a.scale_log2 = float(double(p.sm_scale) * 1.4426950408889634);
   return a;
+}
+
+// Partial states in a caller's float workspace: [max_slots][tile_q][D] outputs, then
+// [max_slots][tile_q] LSEs.
+bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* int_ws, void* float_ws) {
+  float* fw = static_cast<float*>(float_ws);
+  return attn_args(p, t, int_ws, fw, fw ? fw + size_t(p.max_slots) * p.tile_q * p.head_dim : nullptr);
+}
+
+bsk::MergeArgs merge_args(const bsk_problem& p, const bsk_tensors& t, const void* int_ws, const float* part_o,
+                          const float* part_lse) {
+  bsk::MergeArgs a;
+  a.ws = static_cast<const int32_t*>(int_ws);
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.out = t.out;
+  a.o_st = t.o_stride_tok;
+  a.o_sh = t.o_stride_head;
+  a.lse = t.lse;
+  a.lse_st = t.lse_stride_tok;
+  a.group = p.num_qo_heads / p.num_kv_heads;
+  a.out_bf16 = p.out_dtype == BSK_DTYPE_BF16;
+  return a;
+}
+
+// Fixed merge grid: enough blocks for every (entry, row) pair of a full merge table, capped at four
+// per compute unit (the blocks loop; idle blocks only cost their dispatch).
+int merge_grid(const bsk_problem& p) {
+  const int64_t rows_per_block = 256 / (p.head_dim / 4);
+  const int64_t want = (int64_t(p.max_merge) * p.tile_q + rows_per_block - 1) / rows_per_block;
+  return int(want < 1 ? 1 : (want > 1024 ? 1024 : want));
+}
+
+bsk_status launch_run(const bsk_problem& p, const bsk_plan_info& info, const bsk_tensors& t, const bsk::AttnArgs& a,
+                      hipStream_t stream) {
+  hipError_t e;
+  if (p.tile_q == BSK_TILE_DECODE)
+    e = bsk::launch_decode(p.dtype, p.head_dim, p.kv_mode == BSK_KV_DENSE, p.rope_mode, same_kv(p, t), a,
+                           info.num_workers, stream);
+  else if (p.decode_tile_q != 0)
+    e = bsk::launch_mixed(p.head_dim, same_kv(p, t), a, info.num_workers, stream);
+  else
+    e = bsk::launch_prefill(p.head_dim, p.kv_mode == BSK_KV_DENSE, p.tile_q, same_kv(p, t), a, info.num_workers,
+                            stream);
+  if (e != hipSuccess) return hip_fail(e, p.tile_q == BSK_TILE_DECODE ? "decode launch" : "prefill launch");
+  return BSK_OK;
+}
+
+// Checks of the decode-class run beyond check_run_inputs.
+bsk_status check_decode(const bsk_problem* problem) {
+  if (problem->rope_mode != BSK_ROPE_NONE && problem->dtype != BSK_DTYPE_BF16)
+    return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for bf16 only");
+  if (problem->rope_mode != BSK_ROPE_NONE && problem->kv_mode != BSK_KV_PAGED)
+    return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for the paged layout only");
+  return BSK_OK;
+}
+
+// Checks of the prefill-class run beyond check_run_inputs.
+bsk_status check_prefill(const bsk_problem* problem, const bsk_tensors* t) {
+  if (problem->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
+  if (problem->rope_mode != BSK_ROPE_NONE) return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for decode only");
+  // the kernel forms page addresses with a 32 x 32 -> 64-bit multiply of the page id and the byte stride
+  // and keeps a row's head / in-page (dense: in-tile) offset in 32 bits
+  if (problem->kv_mode == BSK_KV_PAGED &&
+      (t->k_stride_page < 0 || t->v_stride_page < 0 || t->k_stride_page > INT32_MAX || t->v_stride_page > INT32_MAX))
+    return fail(BSK_ERR_INVALID_ARG, "page strides must be in [0, 2^31) elements");
+  const int64_t rows = problem->kv_mode == BSK_KV_PAGED ? std::min(problem->page_size, 64) : 64;
+  const int64_t hk = problem->num_kv_heads;
+  const int64_t kspan = (hk - 1) * t->k_stride_head + (rows - 1) * t->k_stride_tok + problem->head_dim;
+  const int64_t vspan = (hk - 1) * t->v_stride_head + (rows - 1) * t->v_stride_tok + problem->head_dim;
+  if (t->k_stride_head < 0 || t->k_stride_tok < 0 || t->v_stride_head < 0 || t->v_stride_tok < 0 ||
+      kspan > INT32_MAX || vspan > INT32_MAX)
+    return fail(BSK_ERR_INVALID_ARG, "head / token strides too large for the prefill kernel's 32-bit row offsets");
+  return BSK_OK;
 }
 
 }  // namespace
@@ -312,48 +395,19 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
 bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                           void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
   bsk_status s = check_run(problem, info, t, int_ws_dev, float_ws, float_ws_bytes, BSK_TILE_DECODE);
+  if (s == BSK_OK) s = check_decode(problem);
   if (s != BSK_OK) return s;
-  if (problem->rope_mode != BSK_ROPE_NONE && problem->dtype != BSK_DTYPE_BF16)
-    return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for bf16 only");
-  if (problem->rope_mode != BSK_ROPE_NONE && problem->kv_mode != BSK_KV_PAGED)
-    return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for the paged layout only");
-  const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
-  hipError_t e = bsk::launch_decode(problem->dtype, problem->head_dim, problem->kv_mode == BSK_KV_DENSE,
-                                    problem->rope_mode, same_kv(*problem, *t), a, info->num_workers,
-                                    static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return BSK_OK;
+  return launch_run(*problem, *info, *t, attn_args(*problem, *t, int_ws_dev, float_ws),
+                    static_cast<hipStream_t>(stream));
 }
 
 bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                            void* int_ws_dev, void* float_ws, size_t float_ws_bytes, void* stream) {
   bsk_status s = check_run(problem, info, t, int_ws_dev, float_ws, float_ws_bytes, BSK_TILE_PREFILL);
+  if (s == BSK_OK) s = check_prefill(problem, t);
   if (s != BSK_OK) return s;
-  if (problem->dtype != BSK_DTYPE_BF16) return fail(BSK_ERR_UNSUPPORTED, "the prefill kernel is bf16 only");
-  if (problem->rope_mode != BSK_ROPE_NONE) return fail(BSK_ERR_UNSUPPORTED, "fused RoPE is built for decode only");
-  // the kernel forms page addresses with a 32 x 32 -> 64-bit multiply of the page id and the byte stride
-  // and keeps a row's head / in-page (dense: in-tile) offset in 32 bits
-  if (problem->kv_mode == BSK_KV_PAGED &&
-      (t->k_stride_page < 0 || t->v_stride_page < 0 || t->k_stride_page > INT32_MAX || t->v_stride_page > INT32_MAX))
-    return fail(BSK_ERR_INVALID_ARG, "page strides must be in [0, 2^31) elements");
-  {
-    const int64_t rows = problem->kv_mode == BSK_KV_PAGED ? std::min(problem->page_size, 64) : 64;
-    const int64_t hk = problem->num_kv_heads;
-    const int64_t kspan = (hk - 1) * t->k_stride_head + (rows - 1) * t->k_stride_tok + problem->head_dim;
-    const int64_t vspan = (hk - 1) * t->v_stride_head + (rows - 1) * t->v_stride_tok + problem->head_dim;
-    if (t->k_stride_head < 0 || t->k_stride_tok < 0 || t->v_stride_head < 0 || t->v_stride_tok < 0 ||
-        kspan > INT32_MAX || vspan > INT32_MAX)
-      return fail(BSK_ERR_INVALID_ARG, "head / token strides too large for the prefill kernel's 32-bit row offsets");
-  }
-  const bsk::AttnArgs a = attn_args(*problem, *t, int_ws_dev, float_ws);
-  hipError_t e =
-      problem->decode_tile_q != 0
-          ? bsk::launch_mixed(problem->head_dim, same_kv(*problem, *t), a, info->num_workers,
-                              static_cast<hipStream_t>(stream))
-          : bsk::launch_prefill(problem->head_dim, problem->kv_mode == BSK_KV_DENSE, problem->tile_q,
-                                same_kv(*problem, *t), a, info->num_workers, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  return BSK_OK;
+  return launch_run(*problem, *info, *t, attn_args(*problem, *t, int_ws_dev, float_ws),
+                    static_cast<hipStream_t>(stream));
 }
 
 bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
@@ -367,23 +421,38 @@ bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* inf
     return fail(BSK_ERR_WORKSPACE, "float workspace missing or smaller than bsk_workspace_query");
   if (!aligned(t->out, problem->out_dtype == BSK_DTYPE_F32 ? 16 : 8) || t->o_stride_tok % 4 || t->o_stride_head % 4)
     return fail(BSK_ERR_INVALID_ARG, "out must be aligned to 4 elements (strides too)");
-  bsk::MergeArgs a;
-  a.ws = static_cast<const int32_t*>(int_ws_dev);
-  a.part_o = static_cast<const float*>(float_ws);
-  a.part_lse = float_ws ? a.part_o + size_t(problem->max_slots) * problem->tile_q * problem->head_dim : nullptr;
-  a.out = t->out;
-  a.o_st = t->o_stride_tok;
-  a.o_sh = t->o_stride_head;
-  a.lse = t->lse;
-  a.lse_st = t->lse_stride_tok;
-  a.group = problem->num_qo_heads / problem->num_kv_heads;
-  a.out_bf16 = problem->out_dtype == BSK_DTYPE_BF16;
-  // fixed grid: enough blocks for every (entry, row) pair of a full merge table, capped at four
-  // per compute unit (the blocks loop; idle blocks only cost their dispatch)
-  const int64_t rows_per_block = 256 / (problem->head_dim / 4);
-  const int64_t want = (int64_t(problem->max_merge) * problem->tile_q + rows_per_block - 1) / rows_per_block;
-  const int grid = int(want < 1 ? 1 : (want > 1024 ? 1024 : want));
-  hipError_t e = bsk::launch_merge(problem->head_dim, a, grid, static_cast<hipStream_t>(stream));
+  const float* fw = static_cast<const float*>(float_ws);
+  const bsk::MergeArgs a =
+      merge_args(*problem, *t, int_ws_dev, fw, fw ? fw + size_t(problem->max_slots) * problem->tile_q * problem->head_dim
+                                                  : nullptr);
+  hipError_t e = bsk::launch_merge(problem->head_dim, a, merge_grid(*problem), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return BSK_OK;
+}
+
+bsk_status bsk_run_noalloc(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                           void* int_ws_dev, void* stream) {
+  bsk_status s = check_run_inputs(problem, info, t, int_ws_dev, problem ? problem->tile_q : 0);
+  if (s == BSK_OK) s = problem->tile_q == BSK_TILE_DECODE ? check_decode(problem) : check_prefill(problem, t);
+  if (s != BSK_OK) return s;
+  void* base = nullptr;
+  size_t bytes = 0;
+  hipError_t e = bsk::noalloc_scratch(&base, &bytes);
+  if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+  // fixed layout per problem shape: [cap][tile_q][D] partial outputs, then [cap][tile_q] LSEs
+  const size_t slot_bytes = size_t(problem->tile_q) * size_t(problem->head_dim + 1) * sizeof(float);
+  const int64_t cap = int64_t(bytes / slot_bytes);
+  if (info->num_slots > cap)
+    return fail(BSK_ERR_CAPACITY, "plan has " + std::to_string(info->num_slots) + " partial-state slots; the " +
+                                      std::to_string(bytes >> 20) + " MiB scratch holds " + std::to_string(cap) +
+                                      " for this tile_q / head_dim (use bsk_run_* with a float workspace)");
+  float* part_o = static_cast<float*>(base);
+  float* part_lse = part_o + size_t(cap) * problem->tile_q * problem->head_dim;
+  s = launch_run(*problem, *info, *t, attn_args(*problem, *t, int_ws_dev, part_o, part_lse),
+                 static_cast<hipStream_t>(stream));
+  if (s != BSK_OK || problem->fused_merge) return s;
+  e = bsk::launch_merge(problem->head_dim, merge_args(*problem, *t, int_ws_dev, part_o, part_lse),
+                        merge_grid(*problem), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return BSK_OK;
 }

@@ -27,6 +27,10 @@ hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t 
 hipError_t launch_merge_pair(const float* oa, const float* la, const float* ob, const float* lb, void* out,
                              float* lse_out, int rows, int D, int out_bf16, hipStream_t stream);
 hipError_t launch_rope_table(float* table, int n_pos, int D, double theta, hipStream_t stream);
+// Device address and size of the no-allocation scratch array on the current device (looked up on
+// the first call per device).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 hipError_t launch_gather(int dtype, int head_dim, bool dense, const AttnArgs& a, const int64_t* row_off, void* k_out,
                          void* v_out, int grid, hipStream_t stream);
 

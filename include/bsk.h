@@ -64,6 +64,9 @@ typedef int32_t bsk_status;
 #define BSK_ROPE_STREAMING 1 /* key position = rank in the query's visible set */
 #define BSK_ROPE_ABSOLUTE 2  /* key position = token index                     */
 
+/* Device scratch of bsk_run_noalloc, held once per GPU the library runs on. */
+#define BSK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
 #define BSK_TILE_DECODE 16       /* query-row tile of bsk_run_decode             */
 #define BSK_TILE_PREFILL 128     /* query-row tiles of bsk_run_prefill: 32 rows  */
 #define BSK_TILE_PREFILL_256 256 /* per wave, four waves (two workgroups per CU) */
@@ -270,6 +273,28 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
  */
 bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                             const void* int_ws_dev, const void* float_ws, size_t float_ws_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory or hold a float workspace:
+ * code under graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Runs what bsk_run_decode (problem->tile_q 16) or
+ * bsk_run_prefill (128, 256) runs, then, unless problem->fused_merge, what
+ * bsk_merge_states runs, with the partial states of split units in a
+ * scratch array the library holds in device memory (BSK_NOALLOC_SCRATCH_BYTES
+ * per GPU, taken when the library's device code is loaded and kept until the
+ * process ends) instead of a caller's float workspace.  Allocates nothing.
+ * The scratch layout is fixed per problem shape (slot stride tile_q rows of
+ * head_dim + 1 floats), so a captured call stays valid after re-planning.
+ * Limit: info->num_slots <= BSK_NOALLOC_SCRATCH_BYTES /
+ * (tile_q * (head_dim + 1) * 4), else BSK_ERR_CAPACITY before anything is
+ * enqueued.  Every call on one GPU uses the same scratch array, which keeps
+ * the last call's partial states (nothing in it needs to start at zero):
+ * calls that overlap in time on one GPU (other streams or threads) race, so
+ * the caller serialises them.  Outputs, the int workspace contract and the
+ * other errors are those of bsk_run_* and bsk_merge_states.
+ */
+bsk_status bsk_run_noalloc(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                           void* int_ws_dev, void* stream);
 
 /*
  * Merge two complete states row by row (the composable format's dense
