@@ -43,6 +43,32 @@ independent implementation can match it bit for bit:
 8. Capacities: more than max_items_per_worker items on a worker, more than
    max_slots slots or more than max_merge merge entries is an error.
 
+Composable format with a shared prefix (shared_prefix_len P > 0): every
+request's KV sequence is one dense prefix of P tokens shared by the whole
+batch, followed by the request's own paged suffix (kv_len counts the suffix
+only; the queries are its last tokens, causal within the suffix, and every
+prefix token is in every query's past).  The FlashInfer paper summary
+[FI-paper, research methodology 1: composable formats] processes the dense
+shared part and the sparse per-request parts separately, each at its own
+block size, and merges their states; here both parts are units of one plan:
+
+   a. Prefix units first, class 2: for each kv head h and each tile_q tile t
+      of the batch's global query rows (request r's rows are the global rows
+      qo_indptr[r]*g + [0, qo_len*g)), rows [t*tile_q, min((t+1)*tile_q, T*g))
+      with T the total query tokens, keys [0, P); r = -1.
+   b. Then the suffix units of the requests, by rules 1-2 (the suffix is a
+      normal request of kv_len keys; window and sinks are not used).
+   c. Chunks, items and costs by rules 3-5 over all units, except that every
+      unit takes partial-state slots (both parts of a row are merged), in unit
+      order.
+   d. Merge table: one entry per suffix unit, in unit order:
+      (r, h, row_lo, row_hi, first_slot, n_chunks, pfx_first, pfx_n), where
+      pfx_n is the chunk count of a prefix unit (the same for all) and
+      pfx_first the first slot of kv head h's first prefix unit.  Row rr of
+      the entry is global row R = qo_indptr[r]*g + row_lo + rr; its prefix
+      partials are row R mod tile_q of slots pfx_first + (R div tile_q)*pfx_n
+      + c, c < pfx_n.  Without a prefix the last two fields are 0.
+
 Pinned by: the partition covers every (unit, visible key) exactly once,
 chunk starts fall on multiples of L_c, the LPT makespan bound, greedy
 optimality of each step, and a committed golden plan (tests).
@@ -79,6 +105,7 @@ class PlanParams:
     window: int = 0
     sink: int = 0
     decode_tile_q: int = 0  # > 0: requests with qo_len * g <= decode_tile_q use one decode-class tile
+    shared_prefix_len: int = 0  # > 0: a dense prefix of this many tokens shared by every request (composable)
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -96,8 +123,18 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
             raise PlanError("INVALID_ARG", "need 0 <= qo_len <= kv_len")
     W = p.num_workers
 
+    P = p.shared_prefix_len
+    if P < 0 or (P > 0 and p.window > 0):
+        raise PlanError("INVALID_ARG", "a shared prefix needs prefix length >= 0 and no sliding window")
     units = []  # (r, h, row_lo, row_hi, lo, hi, sink_hi)
     unit_class = []
+    if P > 0:
+        T = sum(qo_len)
+        for h in range(p.num_kv_heads):
+            for t in range(_ceil_div(T * g, p.tile_q)):
+                units.append((-1, h, t * p.tile_q, min(T * g, (t + 1) * p.tile_q), 0, P, 0))
+                unit_class.append(2)
+    n_prefix_units = len(units)
     for r, (Q, L) in enumerate(zip(qo_len, kv_len)):
         if Q == 0 or L == 0:
             continue
@@ -123,16 +160,24 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
 
     items = []   # (r, h, row_lo, row_hi, kv_lo, kv_hi, slot)
     item_class = []
-    merges = []  # (r, h, row_lo, row_hi, first_slot, n)
+    merges = []  # (r, h, row_lo, row_hi, first_slot, n, pfx_first, pfx_n)
     next_slot = 0
+    prefix_first = {}  # kv head -> first slot of its first prefix unit
+    pfx_n = 0
     for u, (r, h, row_lo, row_hi, lo, hi, sink_hi) in enumerate(units):
         chunks = [(max(lo, k * Lc), min(hi, (k + 1) * Lc)) for k in range(lo // Lc, (hi - 1) // Lc + 1)]
         if sink_hi > 0:
             chunks.append((0, sink_hi))
-        if len(chunks) >= 2:
+        if len(chunks) >= 2 or P > 0:
             first = next_slot
             next_slot += len(chunks)
-            merges.append((r, h, row_lo, row_hi, first, len(chunks)))
+            if u < n_prefix_units:
+                prefix_first.setdefault(h, first)
+                pfx_n = len(chunks)
+            elif P > 0:
+                merges.append((r, h, row_lo, row_hi, first, len(chunks), prefix_first[h], pfx_n))
+            else:
+                merges.append((r, h, row_lo, row_hi, first, len(chunks), 0, 0))
             for c, (a, b) in enumerate(chunks):
                 items.append((r, h, row_lo, row_hi, a, b, first + c))
                 item_class.append(unit_class[u])
@@ -170,6 +215,6 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
         "cost": np.asarray(cost, dtype=np.int64),
         "worker_items": worker_items,
         "load": np.asarray(load, dtype=np.int64),
-        "merge": np.asarray(merges, dtype=np.int64).reshape(-1, 6),
+        "merge": np.asarray(merges, dtype=np.int64).reshape(-1, 8),
         "num_slots": next_slot,
     }

@@ -394,7 +394,8 @@ def test_plan_coverage_and_bounds(causal, window, sink):
     for w, lst in enumerate(plan["worker_items"]):
         assert plan["load"][w] == sum(cost[i] for i in lst)
     # slots: consecutive per multi-chunk unit, matching the merge table
-    for (r, h, rlo, rhi, first, n) in plan["merge"]:
+    for (r, h, rlo, rhi, first, n, pfx_first, pfx_n) in plan["merge"]:
+        assert pfx_first == 0 and pfx_n == 0  # no shared prefix
         its = [it for it in plan["items"] if tuple(it[:4]) == (r, h, rlo, rhi)]
         assert [it[6] for it in its] == list(range(first, first + n))
 
@@ -433,7 +434,99 @@ def test_plan_golden_tiny_decode():
     assert plan["chunk"] == gold["chunk"]
     assert plan["items"].tolist() == gold["items"]
     assert plan["worker_items"] == gold["worker_items"]
-    assert plan["merge"].tolist() == gold["merge"]
+    assert plan["merge"][:, :6].tolist() == gold["merge"]
+    assert (plan["merge"][:, 6:] == 0).all()  # no shared prefix: the prefix fields stay zero
+
+
+def _prefix_params(**kw):
+    base = dict(num_qo_heads=4, num_kv_heads=2, tile_q=4, tile_kv=16, num_workers=8, split_factor=2,
+                min_chunk=16, max_chunk=0, item_overhead=0, max_items_per_worker=64, max_slots=4096,
+                max_merge=4096, causal=True, decode_tile_q=4, shared_prefix_len=70)
+    base.update(kw)
+    return oracle.PlanParams(**base)
+
+
+def test_plan_shared_prefix_hand_derived():
+    """Composable plan with a 70-token shared prefix, worked by hand.
+
+    g = 2; requests qo [1, 2, 1], suffix kv [20, 33, 5]: T = 4 tokens, 8 global rows, so with
+    tile_q = 4 each kv head has two prefix units (rows [0,4) and [4,8)).  Suffix rows 2, 4, 2 fit
+    the 4-row decode tile.  C = 4*70 + 2*(20 + 33 + 5) = 396, L_c = max(16, roundup(ceil(396/16),
+    16)) = 32.  Prefix chunks [0,32) [32,64) [64,70) (pfx_n = 3); suffix chunks r0 [0,20); r1
+    [0,32) [32,33); r2 [0,5).  Slots in unit order: prefix (h0,t0) 0-2, (h0,t1) 3-5, (h1,t0) 6-8,
+    (h1,t1) 9-11; r0h0 12; r0h1 13; r1h0 14,15; r1h1 16,17; r2h0 18; r2h1 19.  Request 1's rows
+    are global rows 2..5: rows 2,3 of prefix tile 0 and rows 0,1 of tile 1."""
+    plan = oracle.plan_ref([1, 2, 1], [20, 33, 5], _prefix_params())
+    assert plan["chunk"] == 32 and plan["total_cost"] == 396 and plan["num_slots"] == 20
+    units = plan["units"].tolist()
+    assert units[:4] == [[-1, 0, 0, 4, 0, 70, 0], [-1, 0, 4, 8, 0, 70, 0], [-1, 1, 0, 4, 0, 70, 0],
+                         [-1, 1, 4, 8, 0, 70, 0]]
+    assert plan["merge"].tolist() == [[0, 0, 0, 2, 12, 1, 0, 3], [0, 1, 0, 2, 13, 1, 6, 3],
+                                      [1, 0, 0, 4, 14, 2, 0, 3], [1, 1, 0, 4, 16, 2, 6, 3],
+                                      [2, 0, 0, 2, 18, 1, 0, 3], [2, 1, 0, 2, 19, 1, 6, 3]]
+    prefix_items = [it for it in plan["items"].tolist() if it[0] == -1]
+    assert [(it[1], it[2], it[4], it[5], it[6]) for it in prefix_items] == [
+        (0, 0, 0, 32, 0), (0, 0, 32, 64, 1), (0, 0, 64, 70, 2), (0, 4, 0, 32, 3), (0, 4, 32, 64, 4),
+        (0, 4, 64, 70, 5), (1, 0, 0, 32, 6), (1, 0, 32, 64, 7), (1, 0, 64, 70, 8), (1, 4, 0, 32, 9),
+        (1, 4, 32, 64, 10), (1, 4, 64, 70, 11)]
+    assert plan["item_class"].tolist().count(2) == 12
+    with pytest.raises(oracle.PlanError):
+        oracle.plan_ref([1], [20], _prefix_params(window=8))
+
+
+@pytest.mark.parametrize("tile_q,W_", [(4, 8), (8, 3), (16, 5)])
+def test_plan_shared_prefix_merge_is_flat_attention(tile_q, W_):
+    """Every item of a composable plan evaluated on its own (oracle.attention_partial over the dense
+    prefix or the request's pages) and merged as its merge record says, rows mapped to prefix tiles
+    through their global rows, equals attention over the flat layout (prefix pages followed by the
+    request's own pages).  Prefix tiles straddle requests' rows; prefix and suffix both split; one
+    request's suffix is tiled by tile_q (class 0), the others are decode-class units."""
+    rng = np.random.default_rng(33)
+    P, Hq, Hk, d, ps = 48, 8, 2, 16, 4
+    qo = np.array([1, 2, 4, 1, 3, 5])    # the last request's 20 rows exceed the 16-row decode tile
+    kv = np.array([9, 30, 4, 17, 25, 12])
+    suf = W.paged_batch(name="s", seed=34, kv_len=kv, qo_len=qo, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=d,
+                        page_size=ps, dtype=W.F32, causal=True)
+    pk = rng.standard_normal((P, Hk, d)).astype(np.float32)
+    pv = rng.standard_normal((P, Hk, d)).astype(np.float32)
+    g = Hq // Hk
+    T = int(qo.sum())
+    plan = oracle.plan_ref(qo, kv, _prefix_params(num_qo_heads=Hq, num_kv_heads=Hk, tile_q=tile_q, num_workers=W_,
+                                                  tile_kv=4, min_chunk=4, max_chunk=8 + 4 * (W_ % 2),
+                                                  decode_tile_q=16, shared_prefix_len=P))
+    assert plan["merge"][:, 5].max() >= 2 and plan["merge"][0, 7] >= 2  # both parts split
+    assert set(plan["item_class"].tolist()) == {0, 1, 2}
+    prefix_kv = DenseKV(pk, pv, np.array([0, P]))
+    kp, vp = suf.physical_pools()
+    sk = PagedKV(kp, vp, suf.kv_page_indptr, suf.kv_page_indices, ps)
+    part = {}
+    for (r, h, rlo, rhi, lo, hi, slot) in plan["items"].tolist():
+        if r < 0:
+            part[slot] = oracle.attention_partial(suf.q, np.array([0, T]), np.array([P]), prefix_kv, Hk,
+                                                  suf.sm_scale, 0, h, rlo, rhi, lo, hi, causal=False)
+        else:
+            part[slot] = oracle.attention_partial(suf.q, suf.qo_indptr, kv, sk, Hk, suf.sm_scale, r, h, rlo, rhi,
+                                                  lo, hi, causal=True)
+    O = np.full((T, Hq, d), np.nan)
+    L = np.full((T, Hq), np.nan)
+    for (r, h, rlo, rhi, first, n, pfx_first, pfx_n) in plan["merge"].tolist():
+        for rr in range(rhi - rlo):
+            R = int(suf.qo_indptr[r]) * g + rlo + rr
+            t, pr = R // tile_q, R % tile_q
+            prefix_tile_rows = [it for it in plan["items"].tolist()
+                                if it[0] < 0 and it[1] == h and it[2] <= R < it[3]]
+            assert {it[6] for it in prefix_tile_rows} == set(range(pfx_first + t * pfx_n, pfx_first + (t + 1) * pfx_n))
+            parts = [(part[first + c][0][rr], part[first + c][1][rr]) for c in range(n)]
+            parts += [(part[pfx_first + t * pfx_n + c][0][pr], part[pfx_first + t * pfx_n + c][1][pr])
+                      for c in range(pfx_n)]
+            o, l = oracle.merge(parts)
+            tok, qh = int(suf.qo_indptr[r]) + (rlo + rr) // g, h * g + (rlo + rr) % g
+            O[tok, qh], L[tok, qh] = o, l
+    # flat layout: the prefix as pages shared by every request, then the request's own pages
+    flat, flat_len = oracle.flat_from_composable(pk, pv, sk, kv)
+    Of, Lf = oracle.attention(suf.q, suf.qo_indptr, flat_len, flat, Hk, suf.sm_scale, causal=True)
+    np.testing.assert_allclose(O, Of, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lf, rtol=0, atol=1e-12)
 
 
 def test_bf16_rounding_matches_torch():

@@ -68,7 +68,7 @@ def assert_same_plan(problem, qo_len, kv_len):
         assert np.array_equal(got["worker_class"][w].astype(np.int64), ref["item_class"][ids] if ids else
                               np.zeros(0, dtype=np.int64)), f"worker {w} tile classes"
     assert (got["item_pad"] == 0).all()
-    assert np.array_equal(got["merge"][:, :6].astype(np.int64), ref["merge"])
+    assert np.array_equal(got["merge"].astype(np.int64), ref["merge"])
     assert info.max_load == int(ref["load"].max()) if len(ref["items"]) else True
     assert np.array_equal(got["qo_indptr"], qo_indptr)
     assert np.array_equal(got["kv_len"], np.asarray(kv_len, dtype=np.int32))
