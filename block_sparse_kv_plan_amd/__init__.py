@@ -43,7 +43,7 @@ class Problem(ctypes.Structure):
                 ("tile_q", i32), ("tile_kv", i32), ("num_workers", i32), ("split_factor", i32),
                 ("min_chunk", i32), ("max_chunk", i32), ("item_overhead", i32), ("max_batch", i32),
                 ("max_items_per_worker", i32), ("max_slots", i32), ("max_merge", i32),
-                ("independent_kv_strides", i32), ("decode_tile_q", i32)]
+                ("independent_kv_strides", i32), ("decode_tile_q", i32), ("shared_prefix_len", i32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -58,7 +58,8 @@ class Tensors(ctypes.Structure):
                 ("v_stride_page", i64), ("v_stride_head", i64), ("v_stride_tok", i64),
                 ("kv_page_indices", vp), ("out", vp), ("o_stride_tok", i64), ("o_stride_head", i64),
                 ("lse", vp), ("lse_stride_tok", i64), ("rope_cos_sin", vp), ("rope_n_pos", i32),
-                ("reserved0", i32)]
+                ("reserved0", i32), ("prefix_k", vp), ("prefix_v", vp), ("prefix_k_stride_tok", i64),
+                ("prefix_k_stride_head", i64), ("prefix_v_stride_tok", i64), ("prefix_v_stride_head", i64)]
 
 
 P = ctypes.POINTER

@@ -32,7 +32,7 @@ def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE
                  sm_scale=None, tile_q=TILE_DECODE, num_workers, tile_kv=None, split_factor=None,
                  min_chunk=None, max_chunk=0, item_overhead=0, max_batch, max_items_per_worker=None,
                  max_slots=None, max_merge=None, fused_merge=0, independent_kv_strides=0,
-                 decode_tile_q=0) -> Problem:
+                 decode_tile_q=0, shared_prefix_len=0) -> Problem:
     d = DEFAULTS[tile_q]
     tile_kv = tile_kv if tile_kv is not None else max(d["tile_kv"], page_size if kv_mode == KV_PAGED else 1)
     kmax = max_items_per_worker if max_items_per_worker is not None else d["max_items_per_worker"]
@@ -53,12 +53,15 @@ def make_problem(*, num_qo_heads, num_kv_heads, head_dim, dtype, out_dtype=DTYPE
     p.max_merge = max_merge if max_merge is not None else num_workers * kmax
     p.independent_kv_strides = independent_kv_strides
     p.decode_tile_q = decode_tile_q
+    p.shared_prefix_len = shared_prefix_len
     return p
 
 
-def tensors_for(problem: Problem, q, k, v, out, lse, page_indices=None, layout: str = "HND", rope=None) -> Tensors:
+def tensors_for(problem: Problem, q, k, v, out, lse, page_indices=None, layout: str = "HND", rope=None,
+                prefix_k=None, prefix_v=None) -> Tensors:
     """Describe torch tensors to the C ABI.  PAGED k/v: [pages, Hk, ps, d] ("HND") or
-    [pages, ps, Hk, d] ("NHD"); DENSE k/v: [N, Hk, d].  q/out: [T, Hq, d]; lse: [T, Hq]."""
+    [pages, ps, Hk, d] ("NHD"); DENSE k/v: [N, Hk, d].  q/out: [T, Hq, d]; lse: [T, Hq].
+    prefix_k / prefix_v: the shared dense prefix [P, Hk, d] of a composable batch."""
     t = Tensors()
     t.q, t.q_stride_tok, t.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
     t.k, t.v = k.data_ptr(), v.data_ptr()
@@ -81,6 +84,11 @@ def tensors_for(problem: Problem, q, k, v, out, lse, page_indices=None, layout: 
     t.lse, t.lse_stride_tok = lse.data_ptr(), lse.stride(0)
     if rope is not None:
         t.rope_cos_sin, t.rope_n_pos = rope.data_ptr(), rope.shape[0]
+    if prefix_k is not None:
+        assert prefix_k.stride(-1) == 1 and prefix_v.stride(-1) == 1, "last dimension must be contiguous"
+        t.prefix_k, t.prefix_v = prefix_k.data_ptr(), prefix_v.data_ptr()
+        t.prefix_k_stride_tok, t.prefix_k_stride_head = prefix_k.stride(0), prefix_k.stride(1)
+        t.prefix_v_stride_tok, t.prefix_v_stride_head = prefix_v.stride(0), prefix_v.stride(1)
     return t
 
 

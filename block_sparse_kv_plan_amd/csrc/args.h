@@ -39,6 +39,10 @@ struct AttnArgs {
   int32_t out_bf16;
   int32_t fused_merge;  // 1: the chunk that completes a split unit merges it in-kernel
   float scale_log2;     // sm_scale * log2(e): logits are kept in base 2
+  // shared dense prefix of a composable batch (class-2 items of the mixed launch)
+  const void* pk;
+  const void* pv;
+  int64_t pk_st, pk_sh, pv_st, pv_sh;
 };
 
 // Launch arguments of the append kernel (new tokens' K/V into the paged cache).

@@ -69,6 +69,12 @@ bsk_status check_problem(const bsk_problem* p) {
     return fail(BSK_ERR_INVALID_ARG, "decode_tile_q must be 0, or 16 with tile_q 128");
   if (p->decode_tile_q != 0 && p->kv_mode != BSK_KV_PAGED)
     return fail(BSK_ERR_UNSUPPORTED, "the mixed launch is built for the paged layout only");
+  if (p->shared_prefix_len < 0) return fail(BSK_ERR_INVALID_ARG, "shared_prefix_len must be >= 0");
+  if (p->shared_prefix_len > 0 &&
+      (p->tile_q != BSK_TILE_PREFILL || p->decode_tile_q != BSK_TILE_DECODE || p->kv_mode != BSK_KV_PAGED))
+    return fail(BSK_ERR_INVALID_ARG, "a shared prefix needs tile_q 128, decode_tile_q 16 and paged suffixes");
+  if (p->shared_prefix_len > 0 && (p->window > 0 || p->rope_mode != BSK_ROPE_NONE || p->fused_merge != 0))
+    return fail(BSK_ERR_UNSUPPORTED, "a shared prefix is built without window, RoPE and in-kernel merge");
   if (p->window > 0 && p->sink < 0) return fail(BSK_ERR_INVALID_ARG, "sink must be >= 0");
   if (p->rope_mode < BSK_ROPE_NONE || p->rope_mode > BSK_ROPE_ABSOLUTE) return fail(BSK_ERR_INVALID_ARG, "rope_mode");
   if (p->rope_mode == BSK_ROPE_STREAMING && !p->causal)
@@ -112,6 +118,7 @@ bsk::PlanParams plan_params(const bsk_problem& p) {
   q.window = p.window > 0 ? p.window : 0;
   q.sink = p.window > 0 ? p.sink : 0;
   q.decode_tile_q = p.decode_tile_q;
+  q.shared_prefix_len = p.shared_prefix_len;
   return q;
 }
 
@@ -152,6 +159,13 @@ bsk_status check_run_inputs(const bsk_problem* p, const bsk_plan_info* info, con
   if (!aligned(t->out, p->out_dtype == BSK_DTYPE_F32 ? 16 : 8) || t->o_stride_tok % 4 || t->o_stride_head % 4)
     return fail(BSK_ERR_INVALID_ARG, "out must be aligned to 4 elements (strides too)");
   if (p->kv_mode == BSK_KV_PAGED && !t->kv_page_indices) return fail(BSK_ERR_INVALID_ARG, "kv_page_indices is NULL");
+  if (p->shared_prefix_len > 0) {
+    if (!t->prefix_k || !t->prefix_v || !aligned(t->prefix_k, 16) || !aligned(t->prefix_v, 16))
+      return fail(BSK_ERR_INVALID_ARG, "prefix_k / prefix_v missing or not 16-byte aligned");
+    if (t->prefix_k_stride_tok % vec || t->prefix_k_stride_head % vec || t->prefix_v_stride_tok % vec ||
+        t->prefix_v_stride_head % vec)
+      return fail(BSK_ERR_INVALID_ARG, "prefix strides must be multiples of 16 bytes");
+  }
   if (p->rope_mode != BSK_ROPE_NONE) {
     if (!t->rope_cos_sin || !aligned(t->rope_cos_sin, 16)) return fail(BSK_ERR_INVALID_ARG, "rope table missing");
     int64_t need = info->max_kv_len;
@@ -200,6 +214,12 @@ bsk::AttnArgs attn_args(const bsk_problem& p, const bsk_tensors& t, const void* 
   a.fused_merge = p.fused_merge != 0;
   a.rope = t.rope_cos_sin;
   a.rope_n_pos = t.rope_n_pos;
+  a.pk = p.shared_prefix_len > 0 ? t.prefix_k : nullptr;
+  a.pv = p.shared_prefix_len > 0 ? t.prefix_v : nullptr;
+  a.pk_st = t.prefix_k_stride_tok;
+  a.pk_sh = t.prefix_k_stride_head;
+  a.pv_st = t.prefix_v_stride_tok;
+  a.pv_sh = t.prefix_v_stride_head;
   a.group = p.num_qo_heads / p.num_kv_heads;
   a.page_shift = p.kv_mode == BSK_KV_PAGED ? ilog2(p.page_size) : 0;
   a.causal = p.causal;
@@ -281,6 +301,14 @@ bsk_status check_prefill(const bsk_problem* problem, const bsk_tensors* t) {
   if (t->k_stride_head < 0 || t->k_stride_tok < 0 || t->v_stride_head < 0 || t->v_stride_tok < 0 ||
       kspan > INT32_MAX || vspan > INT32_MAX)
     return fail(BSK_ERR_INVALID_ARG, "head / token strides too large for the prefill kernel's 32-bit row offsets");
+  if (problem->shared_prefix_len > 0) {
+    // the dense prefix tiles are 64 rows of consecutive tokens
+    const int64_t pks = (hk - 1) * t->prefix_k_stride_head + 63 * t->prefix_k_stride_tok + problem->head_dim;
+    const int64_t pvs = (hk - 1) * t->prefix_v_stride_head + 63 * t->prefix_v_stride_tok + problem->head_dim;
+    if (t->prefix_k_stride_tok < 0 || t->prefix_k_stride_head < 0 || t->prefix_v_stride_tok < 0 ||
+        t->prefix_v_stride_head < 0 || pks > INT32_MAX || pvs > INT32_MAX)
+      return fail(BSK_ERR_INVALID_ARG, "prefix strides too large for the prefill kernel's 32-bit row offsets");
+  }
   return BSK_OK;
 }
 

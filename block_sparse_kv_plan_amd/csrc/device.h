@@ -74,16 +74,23 @@ __device__ __forceinline__ float4 load_part4(const float* p) {
 // Merge of one (row, 4 columns) of a split unit from its chunks' partial
 // states: M = max_c LSE_c, w_c = exp(LSE_c - M), O = sum_c w_c O_c / sum_c w_c,
 // LSE = M + ln sum_c w_c; every chunk empty gives O = 0, LSE = -inf.  Writes
-// the output row (and the LSE when c4 == 0).
+// the output row (and the LSE when c4 == 0).  With a shared prefix
+// (rec[MG_PFX_N] > 0) the row's prefix partials join the chunks: the row is
+// global query row R = q0 * g + row_lo + rr, held as row R % tile_q of the
+// prefix tile R / tile_q of its kv head.
 template <int D, bool COHERENT = false>
 __device__ __forceinline__ void merge_row(const int32_t* rec, int rr, int c4, int tile_q,
                                           const float* __restrict__ part_o, const float* __restrict__ part_lse,
                                           int q0, int g, void* out, int64_t o_st, int64_t o_sh, float* lse_out,
                                           int64_t lse_st, int out_bf16) {
   const int h = rec[MG_H], row_lo = rec[MG_ROW_LO];
-  const int first = rec[MG_FIRST_SLOT], nc = rec[MG_N];
-  const float* pl = part_lse + int64_t(first) * tile_q + rr;
-  const float* po = part_o + (int64_t(first) * tile_q + rr) * D + c4;
+  const int first = rec[MG_FIRST_SLOT], n_own = rec[MG_N], n_pfx = rec[MG_PFX_N];
+  const int nc = n_own + n_pfx;
+  // partial-state rows (slot * tile_q + row) of the row's own chunks and of its prefix chunks
+  const int64_t own0 = int64_t(first) * tile_q + rr;
+  const int64_t R = int64_t(q0) * g + row_lo + rr;
+  const int64_t pfx0 = n_pfx > 0 ? (int64_t(rec[MG_PFX_FIRST]) + (R / tile_q) * n_pfx) * tile_q + R % tile_q : 0;
+  auto part_row = [&](int c) { return c < n_own ? own0 + int64_t(c) * tile_q : pfx0 + int64_t(c - n_own) * tile_q; };
   // chunks in groups of eight: all loads of a group are issued together (one memory latency per
   // group), then the group's maximum moves the running reference and its terms are added
   float M = -INFINITY, wsum = 0.f;
@@ -95,10 +102,10 @@ __device__ __forceinline__ void merge_row(const int32_t* rec, int rr, int c4, in
     for (int k = 0; k < 8; ++k) {
       // past the last chunk: the last chunk's values are read again (always in bounds, so the
       // loads need no predicate) and weighted 0
-      const int c = min(c0 + k, nc - 1);
-      const float l = load_part<COHERENT>(pl + int64_t(c) * tile_q);
+      const int64_t pr = part_row(min(c0 + k, nc - 1));
+      const float l = load_part<COHERENT>(part_lse + pr);
       lc[k] = c0 + k < nc ? l : -INFINITY;
-      x[k] = load_part4<COHERENT>(po + int64_t(c) * tile_q * D);
+      x[k] = load_part4<COHERENT>(part_o + pr * D + c4);
     }
     float gm = lc[0];
 #pragma unroll

@@ -56,7 +56,8 @@ enum : int {
   IT_QLEN = 9,    // the request's query length
   IT_KVLEN = 10,  // the request's kv_len
   IT_KBASE = 11,  // the request's kv_indptr[r]: first page (paged) or token (dense) offset
-  IT_CLASS = 12,  // tile class: 0 = the plan's tile_q, 1 = the decode tile (mixed launches)
+  IT_CLASS = 12,  // tile class: 0 = the plan's tile_q, 1 = the decode tile (mixed launches),
+                  // 2 = the shared dense prefix (r = -1; rows are the batch's global query rows)
   ITEM_WORDS = 16,  // words 13..15 are zero
 };
 
@@ -68,6 +69,8 @@ enum : int {
   MG_ROW_HI = 3,
   MG_FIRST_SLOT = 4,
   MG_N = 5,
+  MG_PFX_FIRST = 6,  // shared prefix: first slot of this kv head's first prefix unit
+  MG_PFX_N = 7,      // shared prefix: chunks per prefix unit (0: no prefix part)
   MERGE_WORDS = 8,
 };
 

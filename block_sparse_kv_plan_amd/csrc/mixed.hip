@@ -20,6 +20,13 @@
 // last chunk, or the separate merge pass) is the one of the large-tile plan.
 // bf16, paged KV, no RoPE; 2 workgroups per CU (the prefill body's register
 // and LDS budget).
+//
+// A composable batch (FlashInfer paper summary, "Research methodology" 1:
+// a dense shared part and sparse per-request parts, each at its own block
+// size) adds a third class: 128-row items of the dense prefix every request
+// shares, over the batch's global query rows, run by the large-tile body on
+// the prefix's own K/V.  Their partial states meet the suffix items' in the
+// merge pass.
 
 #include "decode_item.h"
 #include "launch.h"
@@ -47,11 +54,28 @@ __global__ __launch_bounds__(kPreThreads, 2) void mixed_kernel(AttnArgs a) {
   const int32_t* __restrict__ items = ws + ws[HDR_OFF_ITEMS];
   for (int it = it_begin; it < it_end; ++it) {
     const int32_t* rec = items + int64_t(it) * ITEM_WORDS;
-    if (rec[IT_CLASS] != 0) {
+    const int cls = rec[IT_CLASS];
+    if (cls == 1) {
       __syncthreads();  // the previous item (either class) is done with the shared LDS
       decode_item<__bf16, D, false, ROPE_NONE, SAME>(a, rec, s_mix.dec, s_pages, &s_last, kMixTileQ);
-    } else {
+    } else if (cls == 0) {
       prefill_item<D, false, kMixTileQ / 64, SAME>(a, rec, s_mix.pre, s_pages, &s_last);  // opens with a barrier
+    } else {
+      // the shared dense prefix of a composable batch: the batch's global query rows against the
+      // prefix's own K/V, every prefix key in every query's past (no mask)
+      AttnArgs ap = a;
+      ap.k = a.pk;
+      ap.v = a.pv;
+      ap.k_sp = 0;
+      ap.v_sp = 0;
+      ap.k_st = a.pk_st;
+      ap.k_sh = a.pk_sh;
+      ap.v_st = a.pv_st;
+      ap.v_sh = a.pv_sh;
+      ap.causal = 0;
+      ap.window = 0;
+      ap.sink = 0;
+      prefill_item<D, true, kMixTileQ / 64, false>(ap, rec, s_mix.pre, s_pages, &s_last);
     }
   }
 }

@@ -36,6 +36,19 @@
 //  7. Merge table: one entry per multi-chunk unit, in unit order.
 //  8. More than max_items_per_worker items on a worker, max_slots slots or
 //     max_merge entries is a capacity error (no fallback).
+//
+// Composable batches (shared_prefix_len P > 0; the paper summary's
+// composable formats, "Research methodology" 1): every request's KV is a
+// dense prefix of P tokens shared by the batch, then its own paged suffix of
+// kv_len keys (queries causal within the suffix, the whole prefix in their
+// past).  Prefix units come first -- per kv head, tile_q tiles of the batch's
+// global query rows (request r's rows are qo_indptr[r] * g + [0, qo_len * g)),
+// keys [0, P), tile class 2, r = -1 -- then the suffix units by rules 1-2.
+// Every unit takes partial slots, and each suffix unit's merge entry also
+// names the first slot of its kv head's first prefix unit and the chunk
+// count of a prefix unit: row rr of the entry is global row R = qo_indptr[r]
+// * g + row_lo + rr, whose prefix partials are row R % tile_q of slots
+// first + (R / tile_q) * n + c.
 
 #include "plan.h"
 
@@ -128,6 +141,8 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   if (p.max_chunk < 0 || (p.max_chunk > 0 && (p.max_chunk % p.tile_kv != 0 || p.max_chunk < p.min_chunk)))
     return fail(PLAN_INVALID, "max_chunk must be 0 or a multiple of tile_kv that is >= min_chunk");
   if (p.item_overhead < 0) return fail(PLAN_INVALID, "item_overhead must be >= 0");
+  if (p.shared_prefix_len < 0 || (p.shared_prefix_len > 0 && p.window > 0))
+    return fail(PLAN_INVALID, "a shared prefix needs prefix length >= 0 and no sliding window");
   if (batch < 0 || batch > p.max_batch) return fail(PLAN_INVALID, "batch must be in [0, max_batch]");
   if (batch > 0 && (!qo_indptr || !kv_len || !kv_indptr)) return fail(PLAN_INVALID, "null length array");
   if (!buf) return fail(PLAN_INVALID, "null host workspace");
@@ -147,9 +162,19 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     max_qo = std::max<int32_t>(max_qo, int32_t(Q));
   }
 
-  // 1. units (scratch containers are kept per thread across calls)
+  // 1. units (scratch containers are kept per thread across calls); the shared prefix's first
+  const int32_t P = p.shared_prefix_len;
+  const int64_t T = batch > 0 ? int64_t(qo_indptr[batch]) : 0;
+  if (P > 0 && T * g > INT32_MAX) return fail(PLAN_INVALID, "too many query rows");
   thread_local std::vector<Unit> units;
   units.clear();
+  if (P > 0) {
+    const int32_t rows = int32_t(T * g);
+    for (int32_t h = 0; h < p.num_kv_heads; ++h)
+      for (int32_t t = 0; t < int32_t(ceil_div(rows, p.tile_q)); ++t)
+        units.push_back(Unit{-1, h, t * p.tile_q, std::min(rows, (t + 1) * p.tile_q), 0, P, 0, 2});
+  }
+  const size_t n_prefix_units = units.size();
   for (int32_t r = 0; r < batch; ++r) {
     const int32_t Q = qo_indptr[r + 1] - qo_indptr[r];
     const int32_t L = kv_len[r];
@@ -188,22 +213,33 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
 
   // 4-5. chunks -> items, slots, merge entries
   thread_local std::vector<Item> items;
-  thread_local std::vector<std::array<int32_t, 6>> merges;
+  thread_local std::vector<std::array<int32_t, MERGE_WORDS>> merges;
+  thread_local std::vector<int32_t> prefix_first;  // per kv head: first slot of its first prefix unit
   items.clear();
   merges.clear();
+  prefix_first.assign(size_t(p.num_kv_heads), -1);
+  int32_t prefix_n = 0;
   int64_t next_slot = 0;
   thread_local std::vector<std::pair<int32_t, int32_t>> chunks;
-  for (const Unit& u : units) {
+  for (size_t ui = 0; ui < units.size(); ++ui) {
+    const Unit& u = units[ui];
     chunks.clear();
     for (int64_t k = u.lo / Lc; k <= (int64_t(u.hi) - 1) / Lc; ++k)
       chunks.emplace_back(int32_t(std::max<int64_t>(u.lo, k * Lc)), int32_t(std::min<int64_t>(u.hi, (k + 1) * Lc)));
     if (u.sink_hi > 0) chunks.emplace_back(0, u.sink_hi);
-    const bool split = chunks.size() >= 2;
+    const bool split = chunks.size() >= 2 || P > 0;
     const int64_t first = next_slot;
     if (split) {
       next_slot += int64_t(chunks.size());
       if (next_slot > p.max_slots) return fail(PLAN_CAPACITY, "more partial-state slots than max_slots");
-      merges.push_back({u.r, u.h, u.row_lo, u.row_hi, int32_t(first), int32_t(chunks.size())});
+      if (ui < n_prefix_units) {
+        if (prefix_first[size_t(u.h)] < 0) prefix_first[size_t(u.h)] = int32_t(first);
+        prefix_n = int32_t(chunks.size());
+      } else {
+        const bool pfx = P > 0;
+        merges.push_back({u.r, u.h, u.row_lo, u.row_hi, int32_t(first), int32_t(chunks.size()),
+                          pfx ? prefix_first[size_t(u.h)] : 0, pfx ? prefix_n : 0});
+      }
     }
     for (size_t c = 0; c < chunks.size(); ++c) {
       Item it;
@@ -317,15 +353,22 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
     rec[IT_KV_HI] = it.kv_hi;
     rec[IT_SLOT] = it.slot;
     rec[IT_ID] = id;
-    rec[IT_Q0] = qo_indptr[it.r];
-    rec[IT_QLEN] = qo_indptr[it.r + 1] - qo_indptr[it.r];
-    rec[IT_KVLEN] = kv_len[it.r];
-    rec[IT_KBASE] = kv_indptr[it.r];
+    if (it.r >= 0) {
+      rec[IT_Q0] = qo_indptr[it.r];
+      rec[IT_QLEN] = qo_indptr[it.r + 1] - qo_indptr[it.r];
+      rec[IT_KVLEN] = kv_len[it.r];
+      rec[IT_KBASE] = kv_indptr[it.r];
+    } else {  // shared prefix: the batch's global query rows against the dense prefix
+      rec[IT_Q0] = 0;
+      rec[IT_QLEN] = int32_t(T);
+      rec[IT_KVLEN] = P;
+      rec[IT_KBASE] = 0;
+    }
     rec[IT_CLASS] = it.cls;
   }
   for (size_t m = 0; m < merges.size(); ++m) {
     int32_t* rec = buf + L.off_merge + int64_t(m) * MERGE_WORDS;
-    for (int k = 0; k < 6; ++k) rec[k] = merges[m][k];
+    for (int k = 0; k < MERGE_WORDS; ++k) rec[k] = merges[m][k];
     for (int32_t c = 0; c < merges[m][5]; ++c) buf[L.off_slotmap + merges[m][4] + c] = int32_t(m);
   }
   // arrival counters stay zero (memset above)

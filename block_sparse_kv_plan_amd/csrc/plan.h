@@ -25,6 +25,7 @@ struct PlanParams {
   int32_t window = 0;
   int32_t sink = 0;
   int32_t decode_tile_q = 0;  // > 0: requests with qo_len * g <= decode_tile_q get one decode-class tile
+  int32_t shared_prefix_len = 0;  // > 0: a dense prefix of this many tokens shared by every request
 };
 
 struct PlanStats {

@@ -123,6 +123,18 @@ typedef struct bsk_problem {
      bsk_run_prefill runs both classes in one persistent launch (bf16,
      paged, no RoPE). */
   int32_t decode_tile_q;
+  /* Composable format with a shared prefix ([FI-paper, methodology 1]):
+     0 (off) or P > 0 -- every request's KV sequence is a dense prefix of P
+     tokens shared by the whole batch (bsk_tensors.prefix_k / prefix_v),
+     followed by the request's own paged suffix; kv_len and the page table
+     describe the suffix only, the queries are the suffix's last tokens
+     (causal within it) and every prefix token is in their past.  The plan
+     puts the prefix's 128-row tiles over the batch's query rows and the
+     suffixes' decode / 128-row tiles on the same workers, bsk_run_prefill
+     runs them in one launch and bsk_merge_states combines each row's prefix
+     and suffix partial states.  Needs tile_q 128, decode_tile_q 16, bf16,
+     paged suffixes, no window, no RoPE, fused_merge 0. */
+  int32_t shared_prefix_len;
 } bsk_problem;
 
 /* Filled by bsk_plan; passed unchanged to run/merge. */
@@ -166,6 +178,13 @@ typedef struct bsk_tensors {
   const float* rope_cos_sin; /* [rope_n_pos, d/2, 2] (cos, sin), see bsk_rope_table */
   int32_t rope_n_pos;
   int32_t reserved0;
+  /* shared dense prefix (problem.shared_prefix_len > 0): token j < P of
+     kv head h at prefix_k[j * prefix_k_stride_tok + h * prefix_k_stride_head
+     + c], the same for prefix_v with its own strides; NULL otherwise */
+  const void* prefix_k;
+  const void* prefix_v;
+  int64_t prefix_k_stride_tok, prefix_k_stride_head;
+  int64_t prefix_v_stride_tok, prefix_v_stride_head;
 } bsk_tensors;
 
 /* Human-readable name of a status code (static string). */

@@ -47,9 +47,10 @@ def test_struct_layouts_match_c():
 int main(void) {
   printf("bsk_problem %zu\nbsk_plan_info %zu\nbsk_tensors %zu\n", sizeof(bsk_problem), sizeof(bsk_plan_info),
          sizeof(bsk_tensors));
-  F(bsk_problem, rope_theta) F(bsk_problem, sm_scale) F(bsk_problem, max_merge)
+  F(bsk_problem, rope_theta) F(bsk_problem, sm_scale) F(bsk_problem, max_merge) F(bsk_problem, shared_prefix_len)
   F(bsk_plan_info, total_cost) F(bsk_plan_info, used_bytes)
   F(bsk_tensors, kv_page_indices) F(bsk_tensors, lse_stride_tok) F(bsk_tensors, rope_n_pos)
+  F(bsk_tensors, prefix_k) F(bsk_tensors, prefix_v_stride_head)
   return 0;
 }
 """

@@ -45,7 +45,8 @@ def ref_params(problem):
         min_chunk=problem.min_chunk, max_chunk=effective_max_chunk(problem), item_overhead=problem.item_overhead,
         max_items_per_worker=problem.max_items_per_worker, max_slots=problem.max_slots,
         max_merge=problem.max_merge, causal=bool(problem.causal), window=max(problem.window, 0),
-        sink=problem.sink if problem.window > 0 else 0, decode_tile_q=problem.decode_tile_q)
+        sink=problem.sink if problem.window > 0 else 0, decode_tile_q=problem.decode_tile_q,
+        shared_prefix_len=problem.shared_prefix_len)
 
 
 def assert_same_plan(problem, qo_len, kv_len):
@@ -62,8 +63,11 @@ def assert_same_plan(problem, qo_len, kv_len):
         assert np.array_equal(got["worker_items"][w].astype(np.int64), want), f"worker {w}"
         # the record also carries its request's offsets and lengths, copied from the inputs
         r = got["worker_items"][w][:, 0].astype(np.int64)
+        P, T = problem.shared_prefix_len, int(qo_indptr[-1])
         req = np.stack([qo_indptr[r], qo_indptr[r + 1] - qo_indptr[r], np.asarray(kv_len)[r], kv_indptr[r]], axis=1) \
             if len(r) else np.zeros((0, 4), dtype=np.int64)
+        if len(r):  # shared-prefix items (r = -1): the batch's global query rows against the dense prefix
+            req[r < 0] = [0, T, P, 0]
         assert np.array_equal(got["worker_req"][w].astype(np.int64), req.astype(np.int64)), f"worker {w} request fields"
         assert np.array_equal(got["worker_class"][w].astype(np.int64), ref["item_class"][ids] if ids else
                               np.zeros(0, dtype=np.int64)), f"worker {w} tile classes"
@@ -158,6 +162,45 @@ def test_mixed_plan_classes():
     rows = np.asarray(ref["items"])[:, 3] - np.asarray(ref["items"])[:, 2]
     assert rows[cls == 1].max() <= bsk.TILE_DECODE
     assert rows[cls == 0].max() <= bsk.TILE_PREFILL
+
+
+def composable_problem(W_, P, **kw):
+    return decode_problem(32, 8, 128, W_, tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE, causal=True,
+                          shared_prefix_len=P, **kw)
+
+
+def test_composable_one_launch_plan():
+    """The shared-prefix workload (16384-token dense prefix, 64 branches with one query token each) as
+    one plan: 8 kv heads x 2 prefix tiles of 128 global rows, 512 decode-class suffix units."""
+    s = W.shared_prefix_lengths()
+    p = composable_problem(512, 16384)
+    info, ref = assert_same_plan(p, np.ones(len(s), dtype=np.int64), s)
+    cls = ref["item_class"]
+    assert set(np.unique(cls)) == {1, 2}
+    assert len(ref["merge"]) == 64 * 8 and (ref["merge"][:, 7] > 0).all()
+    assert info.num_slots == len(ref["items"])  # every item writes a partial state
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_composable_plans(seed):
+    rng = np.random.default_rng(2000 + seed)
+    B = int(rng.integers(1, 30))
+    kv = rng.integers(1, 3000, size=B)
+    qo = np.minimum(kv, rng.choice([1, 1, 1, 2, 3, 4, 5, 40], size=B))  # decode-class and 128-row suffixes
+    p = composable_problem(int(rng.integers(1, 90)), int(rng.integers(1, 40000)), tile_kv=64,
+                           split_factor=int(rng.integers(1, 4)), min_chunk=64 * int(rng.integers(1, 5)),
+                           item_overhead=int(rng.integers(0, 40)), max_items_per_worker=4096, max_slots=1 << 20,
+                           max_merge=1 << 20)
+    assert_same_plan(p, qo, kv)
+
+
+def test_composable_requires_the_mixed_launch():
+    for kw in (dict(tile_q=bsk.TILE_PREFILL), dict(tile_q=bsk.TILE_PREFILL_256, decode_tile_q=bsk.TILE_DECODE),
+               dict(tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE, window=64),
+               dict(tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE, fused_merge=1)):
+        p = decode_problem(8, 2, 64, 4, shared_prefix_len=100, **kw)
+        with pytest.raises(bsk.BskError):
+            cpp_plan(p, [1], [10])
 
 
 def test_mixed_class_requires_prefill_tile_and_paged_kv():
