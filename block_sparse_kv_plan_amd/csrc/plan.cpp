@@ -24,8 +24,10 @@
 //  2. Total cost C = sum of (hi - lo) + |sink range| over units.
 //  3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W * split)), tile_kv)),
 //     then min(L_c, max_chunk) if max_chunk > 0.
-//  4. A unit's chunks: [max(lo, k L_c), min(hi, (k+1) L_c)) for
-//     k = lo / L_c .. (hi-1) / L_c, then the non-empty sink range.
+//  4. A unit's chunks: with lo_a = lo rounded down to a multiple of tile_kv,
+//     [max(lo, lo_a + k L_c), min(hi, lo_a + (k+1) L_c)) for
+//     k = 0 .. (hi-1-lo_a) / L_c, then the non-empty sink range (boundaries
+//     stay tile_kv-aligned, and a window of n L_c keys is n chunks).
 //  5. Items in unit order, then chunk order; id = creation index;
 //     cost = keys + item_overhead.  Units with >= 2 chunks take consecutive
 //     partial slots from a global counter; single-chunk units use slot -1.
@@ -224,8 +226,10 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   for (size_t ui = 0; ui < units.size(); ++ui) {
     const Unit& u = units[ui];
     chunks.clear();
-    for (int64_t k = u.lo / Lc; k <= (int64_t(u.hi) - 1) / Lc; ++k)
-      chunks.emplace_back(int32_t(std::max<int64_t>(u.lo, k * Lc)), int32_t(std::min<int64_t>(u.hi, (k + 1) * Lc)));
+    const int64_t lo_a = int64_t(u.lo) / p.tile_kv * p.tile_kv;
+    for (int64_t k = 0; k <= (int64_t(u.hi) - 1 - lo_a) / Lc; ++k)
+      chunks.emplace_back(int32_t(std::max<int64_t>(u.lo, lo_a + k * Lc)),
+                          int32_t(std::min<int64_t>(u.hi, lo_a + (k + 1) * Lc)));
     if (u.sink_hi > 0) chunks.emplace_back(0, u.sink_hi);
     const bool split = chunks.size() >= 2 || P > 0;
     const int64_t first = next_slot;

@@ -26,9 +26,11 @@ independent implementation can match it bit for bit:
 2. Total cost C = sum over units of (hi - lo) + |sink range|.
 3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W*split_factor)), tile_kv)),
    then min(L_c, max_chunk) when max_chunk > 0.
-4. Chunks of a unit: for k = lo // L_c .. (hi-1) // L_c the range
-   [max(lo, k*L_c), min(hi, (k+1)*L_c)) (boundaries at absolute multiples of
-   L_c), then the non-empty sink range as the unit's last chunk.
+4. Chunks of a unit: with lo_a = lo rounded down to a multiple of tile_kv,
+   for k = 0 .. (hi - 1 - lo_a) // L_c the range
+   [max(lo, lo_a + k*L_c), min(hi, lo_a + (k+1)*L_c)) (boundaries at lo_a plus
+   multiples of L_c: aligned to tile_kv, and a window of n*L_c keys is n
+   chunks), then the non-empty sink range as the unit's last chunk.
 5. Items are created in unit order (r, h, t ascending), then chunk order;
    item id = creation index; cost = length + item_overhead.  A unit with
    >= 2 chunks gives its items consecutive partial-state slots from a
@@ -70,7 +72,7 @@ block size, and merges their states; here both parts are units of one plan:
       + c, c < pfx_n.  Without a prefix the last two fields are 0.
 
 Pinned by: the partition covers every (unit, visible key) exactly once,
-chunk starts fall on multiples of L_c, the LPT makespan bound, greedy
+chunk starts fall on lo_a plus multiples of L_c, the LPT makespan bound, greedy
 optimality of each step, and a committed golden plan (tests).
 """
 from __future__ import annotations
@@ -165,7 +167,8 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
     prefix_first = {}  # kv head -> first slot of its first prefix unit
     pfx_n = 0
     for u, (r, h, row_lo, row_hi, lo, hi, sink_hi) in enumerate(units):
-        chunks = [(max(lo, k * Lc), min(hi, (k + 1) * Lc)) for k in range(lo // Lc, (hi - 1) // Lc + 1)]
+        lo_a = lo // p.tile_kv * p.tile_kv
+        chunks = [(max(lo, lo_a + k * Lc), min(hi, lo_a + (k + 1) * Lc)) for k in range((hi - 1 - lo_a) // Lc + 1)]
         if sink_hi > 0:
             chunks.append((0, sink_hi))
         if len(chunks) >= 2 or P > 0:

@@ -374,7 +374,10 @@ def _coverage_check(qo, kv, p, plan):
     Lc = plan["chunk"]
     for it in plan["items"]:
         if not (it[4] == 0 and p.window > 0 and it[5] <= p.sink):
-            assert it[4] % Lc == 0 or it[4] == [u for u in plan["units"] if tuple(u[:4]) == tuple(it[:4])][0][4]
+            lo = [u for u in plan["units"] if tuple(u[:4]) == tuple(it[:4])][0][4]
+            lo_a = lo // p.tile_kv * p.tile_kv  # chunk grid: the unit's first key rounded down to tile_kv
+            assert (it[4] - lo_a) % Lc == 0 or it[4] == lo
+            assert it[4] % p.tile_kv == 0 or it[4] == lo
             assert it[5] - it[4] <= Lc
 
 
@@ -398,6 +401,21 @@ def test_plan_coverage_and_bounds(causal, window, sink):
         assert pfx_first == 0 and pfx_n == 0  # no shared prefix
         its = [it for it in plan["items"] if tuple(it[:4]) == (r, h, rlo, rhi)]
         assert [it[6] for it in its] == list(range(first, first + n))
+
+
+def test_plan_window_chunks_follow_the_unit_start():
+    """A window unit's chunk grid starts at its first key rounded down to tile_kv: a 4096-key window
+    that starts on a 16-key boundary is exactly eight 512-key chunks (plus the sink chunk), one that
+    starts inside a block gets a short first chunk and a tail of fewer than 16 keys."""
+    p = _params(num_qo_heads=8, num_kv_heads=1, num_workers=8, split_factor=1, min_chunk=512, max_chunk=512,
+                tile_kv=16, causal=True, window=4096, sink=4)
+    # query at kv_len - 1: the window starts at kv_len - 4096, i.e. at key 160 and at key 167
+    plan = oracle.plan_ref([1, 1], [4096 + 160, 4096 + 167], p)
+    assert plan["chunk"] == 512
+    by_req = {r: [(int(a), int(b)) for (rr, _, _, _, a, b, _) in plan["items"] if rr == r] for r in (0, 1)}
+    assert by_req[0] == [(160 + 512 * k, 160 + 512 * (k + 1)) for k in range(8)] + [(0, 4)]
+    assert by_req[1] == [(167, 672)] + [(160 + 512 * k, 160 + 512 * (k + 1)) for k in range(1, 8)] + \
+        [(4256, 4263), (0, 4)]
 
 
 def test_plan_greedy_each_step_takes_least_loaded():
