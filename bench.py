@@ -164,13 +164,13 @@ def wall_clock(runner, steps, warmup):
     import torch
     stream = torch.cuda.current_stream()
     copy_stream = torch.cuda.Stream()
-    for i in range(warmup):
-        runner.step(i, stream, copy_stream=copy_stream)
-    torch.cuda.synchronize()
     stamps = np.zeros(steps)
-    gc.collect()
+    gc.collect()  # before the warm-up: a collection takes milliseconds, which the GPU would spend idle
     gc.disable()
     try:
+        for i in range(warmup):
+            runner.step(i, stream, copy_stream=copy_stream)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             runner.step(warmup + i, stream, copy_stream=copy_stream)
