@@ -150,14 +150,33 @@ class Runner:
             a.run(self.tensors[c], stream=stream)
 
 
-def wall_clock(runner, steps, warmup):
+WARM_S = 0.25  # sustained load before a secondary leg's timing (MFMA-bound kernels run ~20% slower for
+               # the first ~50 ms of back-to-back launches while the clock ramps; HBM-bound ones do not)
+
+
+def keep_busy(launch, seconds):
+    """Call launch(i) back to back until `seconds` of wall time have passed, synchronising every
+    eight calls so that the time counted is time the GPU spent busy."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while True:
+        for _ in range(8):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            return
+
+
+def wall_clock(runner, steps, warmup, warm_s=0.0):
     """Wall time per step over `steps` back-to-back steps after `warmup` untimed ones.
 
     Plans are uploaded on a copy stream (off the kernels' queue).  Nothing but the steps runs in
     the timed loop: no timing events (kernel durations come from a separate pass,
     kernel_durations()), and the Python garbage collector is paused, so the loop's contents do
     not depend on `steps`.  Host stamps after each step's submission show whether the host kept
-    ahead of the GPU."""
+    ahead of the GPU.  warm_s > 0 adds that much sustained load after the warm-up steps."""
     import gc
 
     import numpy as np
@@ -168,12 +187,21 @@ def wall_clock(runner, steps, warmup):
     gc.collect()  # before the warm-up: a collection takes milliseconds, which the GPU would spend idle
     gc.disable()
     try:
+        done = [0]
+
+        def one(_):
+            runner.step(done[0], stream, copy_stream=copy_stream)
+            done[0] += 1
+
         for i in range(warmup):
-            runner.step(i, stream, copy_stream=copy_stream)
+            one(i)
+        if warm_s > 0:
+            keep_busy(one, warm_s)
         torch.cuda.synchronize()
+        first = done[0]
         t0 = time.perf_counter()
         for i in range(steps):
-            runner.step(warmup + i, stream, copy_stream=copy_stream)
+            runner.step(first + i, stream, copy_stream=copy_stream)
             stamps[i] = time.perf_counter()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -184,13 +212,16 @@ def wall_clock(runner, steps, warmup):
             "host_submit_us_max": round(float(host.max()), 1), "drain_us": round((t1 - stamps[-1]) * 1e6, 1)}
 
 
-def kernel_durations(runner, reps):
+def kernel_durations(runner, reps, warm_s=0.0):
     """The attention kernel's launch duration from HIP events recorded on its own stream right
     around it, over `reps` launches on the last plans (KV copies rotating as in the timed loop).
-    Runs after the wall-clock loop, so its events never share a queue with it."""
+    Runs after the wall-clock loop, so its events never share a queue with it.  warm_s > 0 first
+    keeps the GPU busy with the same launches for that long."""
     import torch
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    if warm_s > 0:
+        keep_busy(lambda i: runner.attn[i % 2].run(runner.tensors[i % len(runner.tensors)], stream=stream), warm_s)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i in range(3):
         runner.attn[i % 2].run(runner.tensors[i % len(runner.tensors)], stream=stream)
@@ -291,9 +322,7 @@ def ceilings(device):
     a = torch.randn((n, n), device=device).to(torch.bfloat16)
     b = torch.randn((n, n), device=device).to(torch.bfloat16)
     c = torch.empty((n, n), device=device, dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
+    keep_busy(lambda i: torch.matmul(a, b, out=c), WARM_S)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 20
     e0.record(stream)
@@ -364,9 +393,7 @@ def mixed_leg(device, reps):
 
     res = {}
     for label, names in (("one_launch", ["mixed"]), ("two_launches", ["decode", "prefill"])):
-        for _ in range(3):
-            go(names)
-        torch.cuda.synchronize()
+        keep_busy(lambda i: go(names), WARM_S)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for e in evs:
             e[0].record(stream)
@@ -536,8 +563,8 @@ def main():
         b = W.ragged_prefill()
         flops, pairs = prefill_flops(b)
         runner = Runner(b, prefill_tile, copies=1, device=device)
-        m = wall_clock(runner, max(5, args.steps // 10), 3)
-        m.update(kernel_durations(runner, max(10, min(args.steps // 5, 40))))
+        m = wall_clock(runner, max(5, args.steps // 10), 3, warm_s=WARM_S)
+        m.update(kernel_durations(runner, max(10, min(args.steps // 5, 40)), warm_s=WARM_S))
         tf = flops / m["kernel_s_mean"] / 1e12
         secondary["ragged_prefill"] = {
             "workload": "ragged_causal_prefill_append_bf16: 16 requests, q lognormal [128,4096] after "
@@ -616,14 +643,20 @@ def main():
         ab = {}
         for name, make, tq, kw in stride_cases(prefill_tile):
             b = make()
-            us = []
-            for ind in (0, 1):
-                runner = Runner(b, tq, copies=2, device=device, independent_kv_strides=ind, **kw)
+            runners = [Runner(b, tq, copies=2, device=device, independent_kv_strides=ind, **kw) for ind in (0, 1)]
+            for runner in runners:
                 for a in runner.attn:
                     a.plan(b.qo_indptr, b.kv_len, runner.kv_indptr, stream=torch.cuda.current_stream())
-                us.append(kernel_durations(runner, 30 if tq == bsk.TILE_DECODE else 10)["kernel_s_mean"] * 1e6)
-                del runner
-                torch.cuda.empty_cache()
+            # the two variants alternate in three rounds after sustained load, so neither sees a colder GPU
+            reps = 10 if tq == bsk.TILE_DECODE else 4
+            tot = [0.0, 0.0]
+            for rnd in range(3):
+                for v, runner in enumerate(runners):
+                    tot[v] += kernel_durations(runner, reps, warm_s=WARM_S if rnd == 0 and v == 0 else 0.0)[
+                        "kernel_s_mean"]
+            us = [t / 3 * 1e6 for t in tot]
+            del runners
+            torch.cuda.empty_cache()
             ab[name] = {"equal_strides_us": round(us[0], 2), "independent_strides_us": round(us[1], 2),
                         "speedup": round(us[1] / us[0], 4)}
             log(f"  strides {name}: {us[1] / us[0]:.4f}x")
@@ -645,8 +678,8 @@ def main():
         rplan = {"split_factor": 2}
         rkw = dict(rplan) if args.fused_merge is None else dict(rplan, fused_merge=args.fused_merge)
         runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, graphs=bool(args.graph), **rkw)
-        m = wall_clock(runner, args.steps, args.warmup)
-        m.update(kernel_durations(runner, max(20, min(args.steps, 100))))
+        m = wall_clock(runner, args.steps, args.warmup, warm_s=WARM_S)
+        m.update(kernel_durations(runner, max(20, min(args.steps, 100)), warm_s=WARM_S))
         secondary["streaming_rope_decode"] = {
             "workload": "streaming_rope_window_sink_decode_bf16: batch 8, kv uniform [32768,131072], 64q/8kv, "
                         "d128, window 4096 + 4 sinks, RoPE theta 5e5 in-kernel",
@@ -709,9 +742,7 @@ def main():
         copies = 3  # 3 x 218 MB of K/V rotate, so no repetition finds the last one's in the 256 MB Infinity Cache
 
         def gpu_us(step):
-            for i in range(3):
-                step(i)
-            torch.cuda.synchronize()
+            keep_busy(step, WARM_S)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for i in range(n):
@@ -748,13 +779,15 @@ def main():
             del pre, suf
             torch.cuda.empty_cache()
         # one launch: the prefix's 128-row items and the suffixes' decode items planned together and run
-        # on one persistent grid, then one merge pass (shared_prefix_len)
+        # on one persistent grid, then one merge pass (shared_prefix_len). Two target chunks per worker
+        # make L_c 1024, which splits the 16384-key prefix into 16 equal chunks; one gives L_c 1152 and a
+        # 256-key tail chunk per prefix tile (measured 57-58 against 60 us per launch)
         from block_sparse_kv_plan_amd.attention import BatchAttention, tensors_for
         from workloads.device import upload
         one_attn = BatchAttention.create(device=device, num_qo_heads=32, num_kv_heads=8, head_dim=128,
                                          dtype=bsk.DTYPE_BF16, page_size=16, causal=True, max_batch=64,
                                          tile_q=bsk.TILE_PREFILL, decode_tile_q=bsk.TILE_DECODE,
-                                         shared_prefix_len=16384)
+                                         shared_prefix_len=16384, split_factor=2)
         du = [upload(c.suffix, device=device) for _ in range(copies)]
         pkv = [(torch.from_numpy(c.prefix.dense_k).to(torch.bfloat16).to(device),
                 torch.from_numpy(c.prefix.dense_v).to(torch.bfloat16).to(device)) for _ in range(copies)]

@@ -32,9 +32,9 @@
 //     cost = keys + item_overhead.  Units with >= 2 chunks take consecutive
 //     partial slots from a global counter; single-chunk units use slot -1.
 //  6. Longest-processing-time assignment: items sorted by (cost desc, id
-//     asc); a min-heap of (load, worker) starting at (0, w); each item pops
-//     the lexicographic minimum, is appended to that worker's list, and
-//     (load + cost, worker) is pushed back.
+//     asc); a priority queue of (load, worker) starting at (0, w); each item
+//     takes the lexicographic minimum, is appended to that worker's list,
+//     and (load + cost, worker) is pushed back.
 //  7. Merge table: one entry per multi-chunk unit, in unit order.
 //  8. More than max_items_per_worker items on a worker, max_slots slots or
 //     max_merge entries is a capacity error (no fallback).
@@ -57,8 +57,6 @@
 #include <algorithm>
 #include <array>
 #include <cstring>
-#include <functional>
-#include <queue>
 #include <utility>
 #include <vector>
 
@@ -69,7 +67,7 @@ namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kWorkerBits = 20;  // the LPT heap packs (load, worker) into 64 bits
+constexpr int kWorkerBits = 20;  // the LPT assignment packs (load, worker) into 64 bits
 constexpr uint64_t kWorkerMask = (uint64_t(1) << kWorkerBits) - 1;
 inline int64_t align4(int64_t x) { return (x + 3) & ~int64_t(3); }
 
@@ -100,22 +98,21 @@ struct Item {
   int64_t cost;
 };
 
-// Binary min-heap of unique 64-bit keys with a combined pop-and-push: the
-// root is replaced by a larger key and sifted down (child choice is
-// branch-free; the key usually sinks to the bottom, so the exit test is
-// well predicted).
-inline void sift_down(uint64_t* h, int32_t n, int32_t i) {
-  const uint64_t key = h[i];
-  for (;;) {
-    int32_t c = 2 * i + 1;
-    if (c >= n) break;
-    const int32_t c2 = c + 1;
-    c += (c2 < n) & (h[c2 < n ? c2 : c] < h[c]);
-    if (h[c] >= key) break;
-    h[i] = h[c];
-    i = c;
+// Winner tree over unique 64-bit keys: leaves t[n + w] (n a power of two,
+// padding leaves at UINT64_MAX), every inner node the smaller of its two
+// children, so t[1] is the minimum.  Raising one leaf recomputes the path to
+// the root.  The path is fixed by the leaf index, so the sibling loads are
+// independent of each other and only the comparisons form a chain (a binary
+// heap's sift-down chains its loads instead, one per level).
+inline void raise_leaf(uint64_t* t, int32_t n, int32_t w, uint64_t key) {
+  int32_t i = n + w;
+  t[i] = key;
+  while (i > 1) {
+    const uint64_t sib = t[i ^ 1];
+    key = sib < key ? sib : key;
+    i >>= 1;
+    t[i] = key;
   }
-  h[i] = key;
 }
 
 }  // namespace
@@ -266,7 +263,7 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   // 6. LPT assignment (flat arrays; the per-worker lists are built as CSR
   //    afterwards, each in assignment order)
   thread_local std::vector<int32_t> order, assign, counts, bucket;
-  thread_local std::vector<uint64_t> heap;
+  thread_local std::vector<uint64_t> tree;
   const int32_t n_items = int32_t(items.size());
   // order = items by (cost desc, id asc): a stable counting sort on cost
   // (costs are bounded by the chunk length plus the overhead)
@@ -288,7 +285,7 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   load.assign(W, 0);
   // All workers start at load 0 and ties go to the lower worker, so the
   // leading run of items with the largest cost is dealt round-robin: after
-  // every full round all loads are equal again.  Exactly what the heap
+  // every full round all loads are equal again.  Exactly what the queue
   // would produce, without its per-item cost.
   int32_t k = 0;
   if (n_items > 0) {
@@ -301,20 +298,24 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
       ++k;
     }
   }
-  // the rest: min-heap of (load, worker) packed as load << 20 | worker, so one
-  // integer comparison gives the lexicographic (load, worker) order
-  heap.resize(W);
-  for (int32_t w = 0; w < W; ++w) heap[w] = (uint64_t(load[w]) << kWorkerBits) | uint64_t(w);
-  std::make_heap(heap.begin(), heap.end(), std::greater<uint64_t>());
+  // the rest: each item goes to the worker with the smallest (load, worker),
+  // kept as load << 20 | worker so that one integer comparison gives the
+  // lexicographic order, in a winner tree over the workers
+  int32_t leaves = 1;
+  while (leaves < W) leaves *= 2;
+  tree.assign(size_t(2 * leaves), ~uint64_t(0));
+  for (int32_t w = 0; w < W; ++w) tree[size_t(leaves + w)] = (uint64_t(load[w]) << kWorkerBits) | uint64_t(w);
+  for (int32_t i = leaves - 1; i >= 1; --i)
+    tree[size_t(i)] = std::min(tree[size_t(2 * i)], tree[size_t(2 * i + 1)]);
   for (; k < n_items; ++k) {
-    const uint64_t top = heap[0];
+    const uint64_t top = tree[1];
     const int32_t w = int32_t(top & kWorkerMask);
     const int32_t id = order[k];
     assign[k] = w;
     ++counts[w];
-    heap[0] = top + (uint64_t(items[id].cost) << kWorkerBits);
-    load[w] = int64_t(heap[0] >> kWorkerBits);
-    sift_down(heap.data(), W, 0);
+    const uint64_t key = top + (uint64_t(items[id].cost) << kWorkerBits);
+    load[w] = int64_t(key >> kWorkerBits);
+    raise_leaf(tree.data(), leaves, w, key);
   }
   int32_t max_on_worker = 0;
   for (int32_t w = 0; w < W; ++w) max_on_worker = std::max(max_on_worker, counts[w]);
@@ -323,7 +324,10 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
 
   // 7. serialise
   const Layout L = layout_for(W, int64_t(items.size()), int64_t(merges.size()), next_slot, batch);
-  std::memset(buf, 0, size_t(L.total_words) * sizeof(int32_t));
+  // every word is written below; zeroed here are the header's padding before the items, and the
+  // slot map (prefix slots belong to no merge entry) and the arrival counters after the arrays
+  std::memset(buf, 0, size_t(L.off_items) * sizeof(int32_t));
+  std::memset(buf + L.off_slotmap, 0, size_t(L.total_words - L.off_slotmap) * sizeof(int32_t));
   buf[HDR_NUM_ITEMS] = int32_t(items.size());
   buf[HDR_NUM_MERGE] = int32_t(merges.size());
   buf[HDR_NUM_SLOTS] = int32_t(next_slot);
@@ -369,13 +373,13 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
       rec[IT_KBASE] = 0;
     }
     rec[IT_CLASS] = it.cls;
+    for (int w = IT_CLASS + 1; w < ITEM_WORDS; ++w) rec[w] = 0;
   }
   for (size_t m = 0; m < merges.size(); ++m) {
     int32_t* rec = buf + L.off_merge + int64_t(m) * MERGE_WORDS;
     for (int k = 0; k < MERGE_WORDS; ++k) rec[k] = merges[m][k];
     for (int32_t c = 0; c < merges[m][5]; ++c) buf[L.off_slotmap + merges[m][4] + c] = int32_t(m);
   }
-  // arrival counters stay zero (memset above)
   for (int32_t r = 0; r <= batch; ++r) buf[L.off_qo + r] = batch ? qo_indptr[r] : 0;
   for (int32_t r = 0; r < batch; ++r) buf[L.off_kvlen + r] = kv_len[r];
   for (int32_t r = 0; r <= batch; ++r) buf[L.off_kvind + r] = batch ? kv_indptr[r] : 0;

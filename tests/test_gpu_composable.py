@@ -62,11 +62,12 @@ def flat_reference(suffix, prefix_k, prefix_v):
 
 def test_shared_prefix_one_launch_full():
     """16384-token dense prefix + 64 paged suffixes uniform [128, 1024], one query token each: the
-    benchmarked one-launch plan (default workers), every token and head against oracle.composable."""
+    benchmarked one-launch plan (default workers, two target chunks per worker), every token and head
+    against oracle.composable."""
     c = W.shared_prefix()
     pre, suf = c.prefix, c.suffix
     say("composable one launch: 16384-token prefix, 64 branches")
-    O, L, info = run_one_launch(suf, pre.dense_k, pre.dense_v)
+    O, L, info = run_one_launch(suf, pre.dense_k, pre.dense_v, split_factor=2)
     assert info.num_merge == 64 * 8
     ref = oracle.composable(suf.q, DenseKV(pre.dense_k, pre.dense_v, pre.kv_indptr), 16384,
                             oracle_kv(suf, physical=True), suf.kv_len, suf.num_kv_heads, suf.sm_scale)
