@@ -413,9 +413,21 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
   info->max_load = st.max_load;
   info->used_bytes = st.used_bytes;
   if (int_ws_dev) {
-    hipError_t e = hipMemcpyAsync(int_ws_dev, host_ws, size_t(st.used_bytes), hipMemcpyHostToDevice,
+    // Pinned host memory has a device address: a kernel on `stream` copies the plan from there
+    // (one launch, ordered with the caller's kernels).  Other host memory goes through
+    // hipMemcpyAsync.
+    void* src_dev = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&src_dev, host_ws, 0);
+    if (e == hipSuccess && src_dev && aligned(src_dev, 16) && aligned(int_ws_dev, 16)) {
+      e = bsk::launch_plan_upload(src_dev, int_ws_dev, st.used_bytes / int64_t(sizeof(int32_t)),
                                   static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+      if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
+    } else {
+      (void)hipGetLastError();  // a pointer that is not pinned host memory is not an error here
+      e = hipMemcpyAsync(int_ws_dev, host_ws, size_t(st.used_bytes), hipMemcpyHostToDevice,
+                         static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+    }
   }
   return BSK_OK;
 }

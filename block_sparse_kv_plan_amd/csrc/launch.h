@@ -26,6 +26,9 @@ hipError_t launch_append(int dtype, int head_dim, const AppendArgs& a, hipStream
 hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t stream);
 hipError_t launch_merge_pair(const float* oa, const float* la, const float* ob, const float* lb, void* out,
                              float* lse_out, int rows, int D, int out_bf16, hipStream_t stream);
+// Copies `words` 32-bit words from a pinned host buffer's device address into device memory, on
+// `stream`; both pointers 16-byte aligned.
+hipError_t launch_plan_upload(const void* src_dev, void* dst, int64_t words, hipStream_t stream);
 hipError_t launch_rope_table(float* table, int n_pos, int D, double theta, hipStream_t stream);
 // Device address and size of the no-allocation scratch array on the current device (looked up on
 // the first call per device).

@@ -1,4 +1,4 @@
-// Partial-state merge, RoPE table and the gather test hook.
+// Partial-state merge, plan upload, RoPE table and the gather test hook.
 //
 // Split-KV (FlashInfer 0.6 wiki, "Kernel types": the split_kv decode path)
 // leaves one (O_c, LSE_c) per key chunk; the exact combination is
@@ -122,7 +122,28 @@ __global__ __launch_bounds__(256) void gather_kernel(AttnArgs a, const int64_t* 
   }
 }
 
+// Plan upload: the plan's words copied from the pinned host buffer (read through its device
+// mapping) into the int workspace, by a kernel on the caller's stream.  Sixteen bytes per thread;
+// both buffers are 16-byte aligned (the host checks), the last thread takes the ragged tail.
+__global__ __launch_bounds__(256) void plan_upload_kernel(const uint32_t* __restrict__ src,
+                                                          uint32_t* __restrict__ dst, int64_t words) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= words) {
+    *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
+  } else {
+    for (int64_t k = i; k < words; ++k) dst[k] = src[k];
+  }
+}
+
 // ---------------------------------------------------------------- host launchers
+
+hipError_t launch_plan_upload(const void* src_dev, void* dst, int64_t words, hipStream_t stream) {
+  const int64_t grid = (words + 1023) / 1024;
+  if (grid < 1 || grid > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_upload_kernel, dim3(unsigned(grid)), dim3(256), 0, stream,
+                     static_cast<const uint32_t*>(src_dev), static_cast<uint32_t*>(dst), words);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t stream) {
   if (head_dim == 128)

@@ -233,9 +233,11 @@ bsk_status bsk_workspace_query(const bsk_problem* problem, size_t* int_ws_bytes,
  * The exact rules, tie-breaks included, are spelled out at the top of
  * csrc/plan.cpp.
  * host_ws receives the plan; if int_ws_dev is non-NULL its first used_bytes
- * are then copied there with one hipMemcpyAsync on `stream` (host_ws must
- * stay untouched until that copy completes).  int_ws_dev == NULL plans on
- * the host only (no GPU needed).
+ * are then copied there on `stream`: by one small kernel that reads host_ws
+ * through its device address when host_ws is pinned host memory
+ * (hipHostMalloc, torch's pin_memory) and both buffers are 16-byte aligned,
+ * else by one hipMemcpyAsync.  host_ws must stay untouched until that copy
+ * completes.  int_ws_dev == NULL plans on the host only (no GPU needed).
  * Errors: INVALID_ARG (inconsistent lengths, bad parameters), CAPACITY
  * (more items on a worker, slots or merge entries than allowed),
  * WORKSPACE (buffers too small), HIP.
