@@ -423,7 +423,7 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
                                   static_cast<hipStream_t>(stream));
       if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
     } else {
-      (void)hipGetLastError();  // a pointer that is not pinned host memory is not an error here
+      if (e != hipSuccess) (void)hipGetLastError();  // not pinned host memory: not an error here
       e = hipMemcpyAsync(int_ws_dev, host_ws, size_t(st.used_bytes), hipMemcpyHostToDevice,
                          static_cast<hipStream_t>(stream));
       if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
