@@ -5,6 +5,7 @@ memory, pinned host memory and streams; all compute is in libbsk's kernels.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional
 
@@ -16,6 +17,55 @@ from . import (DTYPE_BF16, DTYPE_F32, KV_DENSE, KV_PAGED, ROPE_NONE, TILE_DECODE
                run_prefill, workspace_query)
 
 TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
+
+_HIP_EVENT_DISABLE_TIMING = 0x2
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime torch has loaded (same soname, so the same library and device state)."""
+    global _hip
+    if _hip is None:
+        lib = ctypes.CDLL("libamdhip64.so")
+        for name in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventSynchronize", "hipEventDestroy"):
+            getattr(lib, name).restype = ctypes.c_int
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip = lib
+    return _hip
+
+
+class _HostOrderEvent:
+    """A HIP event that only orders the host after GPU work (workspace reuse): created without
+    timing and without the system-scope fence, so recording it does not make the queue write back
+    its caches for the host, which a torch event does (a few microseconds of GPU time per record).
+    Never used to read results on the host or to order another queue."""
+
+    def __init__(self):
+        self._lib = _hip_runtime()
+        ev = ctypes.c_void_p()
+        err = self._lib.hipEventCreateWithFlags(ctypes.byref(ev),
+                                                _HIP_EVENT_DISABLE_TIMING | _HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if err != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({err})")
+        self._ev = ev
+
+    def record(self, stream):
+        err = self._lib.hipEventRecord(self._ev, ctypes.c_void_p(stream.cuda_stream))
+        if err != 0:
+            raise RuntimeError(f"hipEventRecord failed ({err})")
+
+    def synchronize(self):
+        err = self._lib.hipEventSynchronize(self._ev)
+        if err != 0:
+            raise RuntimeError(f"hipEventSynchronize failed ({err})")
+
+    def __del__(self):
+        if getattr(self, "_ev", None) is not None and self._lib is not None:
+            self._lib.hipEventDestroy(self._ev)
 
 # Plan defaults per query-tile class: (tile_kv, split_factor, min_chunk, max_items_per_worker).
 # Decode: one chunk per worker on average; each further item costs a few microseconds of start-up,
@@ -108,14 +158,20 @@ class BatchAttention:
         self.float_ws = torch.empty(max(float_b, 16), dtype=torch.uint8, device=self.device)
         self.host_ws = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
         self.info: Optional[PlanInfo] = None
-        self._uploaded = torch.cuda.Event()   # the plan copy out of host_ws has completed
-        self._consumed = torch.cuda.Event()   # the last run reading int_ws has completed
-        self._merged = torch.cuda.Event()     # the last merge reading int_ws / float_ws has completed
+        self._uploaded = torch.cuda.Event()   # the plan copy out of host_ws has completed (recorded lazily)
+        self._consumed = _HostOrderEvent()    # the last run reading int_ws has completed
+        self._merged = _HostOrderEvent()      # the last merge reading int_ws / float_ws has completed
         self._consumed_stream = None
         self._merged_stream = None
         self._run_stream = None  # stream of a run(merge=False) whose merge() has not been called yet
         self._upload_pending = False
         self._upload_stream = None
+        # An event recorded on the kernels' queue costs GPU time (it ends in a release the host can
+        # see), so the upload gets one only when something needs it: a run on another stream, or
+        # the next plan when no merge on the upload's own stream (whose event comes later in that
+        # stream) has been recorded since.
+        self._upload_recorded = False
+        self._upload_covered = False
 
     @classmethod
     def create(cls, *, device="cuda", num_workers=None, **kw):
@@ -123,9 +179,18 @@ class BatchAttention:
             num_workers = device_workers(make_problem(num_workers=1, **kw))
         return cls(make_problem(num_workers=num_workers, **kw), device=device)
 
+    def _record_upload(self):
+        if not self._upload_recorded:
+            self._uploaded.record(self._upload_stream)
+            self._upload_recorded = True
+
     def plan(self, qo_indptr, kv_len, kv_indptr, stream=None, copy_stream=None) -> PlanInfo:
-        if self._upload_pending:
-            self._uploaded.synchronize()  # host_ws is still being read by the previous copy
+        if self._upload_pending:  # host_ws may still be read by the previous upload
+            if self._upload_covered:
+                self._merged.synchronize()  # recorded after it on the same stream
+            else:
+                self._record_upload()
+                self._uploaded.synchronize()
         stream = stream or torch.cuda.current_stream(self.device)
         up = copy_stream if copy_stream is not None else stream
         self._settle_run()
@@ -145,9 +210,10 @@ class BatchAttention:
                 ev.synchronize()
         self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
                          self.host_ws, self.int_ws, up)
-        self._uploaded.record(up)
         self._upload_pending = True
         self._upload_stream = up
+        self._upload_recorded = False
+        self._upload_covered = False
         return self.info
 
     def run(self, tensors: Tensors, stream=None, merge: bool = True, wait_upload: bool = True):
@@ -156,6 +222,7 @@ class BatchAttention:
         caller (who must have made `stream` wait for the upload already)."""
         stream = stream or torch.cuda.current_stream(self.device)
         if wait_upload and self._upload_stream is not None and self._upload_stream != stream:
+            self._record_upload()
             stream.wait_event(self._uploaded)
         if self.problem.tile_q == TILE_DECODE:
             run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
@@ -202,11 +269,13 @@ class BatchAttention:
         next plan's reuse checks."""
         stream = stream or torch.cuda.current_stream(self.device)
         if self._upload_stream is not None and self._upload_stream != stream:
+            self._record_upload()
             stream.wait_event(self._uploaded)
         with torch.cuda.stream(stream):
             graph.replay()
         self._merged.record(stream)
         self._merged_stream = stream
+        self._upload_covered = self._upload_pending and self._upload_stream == stream
         self._consumed_stream = None
         self._run_stream = None
 
@@ -220,6 +289,7 @@ class BatchAttention:
         merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         self._merged.record(stream)
         self._merged_stream = stream
+        self._upload_covered = self._upload_pending and self._upload_stream == stream
         self._run_stream = None
 
 

@@ -197,7 +197,8 @@ const char* bsk_last_error(void);
  * Persistent-grid size for `problem` on the current device: compute units
  * times the workgroups of the exact kernel variant the problem selects
  * (query-tile class, dtype, head_dim, KV layout, RoPE mode) that fit on one
- * CU at once.  The persistent grid must not exceed what is co-resident (a
+ * CU at once, at most two for the 16-row decode class (three fit, two were
+ * measured faster).  The persistent grid must not exceed what is co-resident (a
  * persistent launch larger than that is what [FI-PR5329, review] reports
  * failing; here it would run a second, unbalanced wave of workers).
  * Only the shape fields of `problem` are read; plan fields may be unset.
