@@ -24,10 +24,12 @@ _hip = None
 
 
 def _hip_runtime():
-    """The HIP runtime torch has loaded (same soname, so the same library and device state)."""
+    """The HIP runtime torch has loaded: opened by its soname, which the dynamic loader matches
+    against the libraries already in the process (torch's copy), so events and streams share
+    one runtime and device state."""
     global _hip
     if _hip is None:
-        lib = ctypes.CDLL("libamdhip64.so")
+        lib = ctypes.CDLL("libamdhip64.so.7")
         for name in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventSynchronize", "hipEventDestroy"):
             getattr(lib, name).restype = ctypes.c_int
         lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]

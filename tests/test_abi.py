@@ -140,3 +140,14 @@ def test_run_rejects_the_same_inputs():
     bad = _clone(info)
     bad.num_workers = 3
     assert run(bad, fake, float_b) == bsk.ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_in_the_process():
+    """The library and the binding's host-ordering events use the HIP runtime torch loaded: after
+    both are opened only one copy of it is mapped (a second copy would not know torch's streams)."""
+    import torch  # noqa: F401
+    from block_sparse_kv_plan_amd.attention import _hip_runtime
+    _hip_runtime()
+    with open("/proc/self/maps") as f:
+        mapped = {line.split()[-1] for line in f if "amdhip64" in line}
+    assert len(mapped) == 1, mapped
