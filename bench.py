@@ -352,8 +352,47 @@ def ceilings(device):
     s = e0.elapsed_time(e1) * 1e-3 / reps
     out["copy_2gib_gbs"] = round(2 * src.numel() / s / 1e9, 1)
     out["copy_frac_of_peak"] = round(2 * src.numel() / s / 1e9 / HBM_PEAK_GBS, 4)
-    out["note"] = "GEMM: 2 n^3 flop per torch.matmul, n = 8192; copy: 2 GiB read + 2 GiB written per copy"
-    del src, dst
+    del dst
+    # streaming read: the library's read hook (every 16-byte piece once, non-temporal loads), best of
+    # three grid sizes
+    import block_sparse_kv_plan_amd as bsk
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    best = 0.0
+    for per_cu in (4, 8, 16):
+        grid = cus * per_cu
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=device)
+        keep_busy(lambda i: bsk.debug_stream_read(src, sink, grid, stream), 0.05)
+        e0.record(stream)
+        for _ in range(reps):
+            bsk.debug_stream_read(src, sink, grid, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3 / reps
+        if src.numel() / s / 1e9 > best:
+            best, best_grid = src.numel() / s / 1e9, grid
+    out["read_2gib_gbs"] = round(best, 1)
+    out["read_frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
+    out["read_grid"] = best_grid
+    # the same read over the Llama-3 decode's algorithmic bytes (one launch of that size, with its
+    # fixed start and drain), three disjoint slices of the buffer in turn (each read last two launches
+    # earlier, 1.4 GB before: not in the 256 MB Infinity Cache)
+    nb = 695809520 // 16 * 16
+    sink = torch.empty(best_grid * 256, dtype=torch.int32, device=device)
+    views = [src[k * 664 * 2**20:k * 664 * 2**20 + nb] for k in range(3)]  # 664 MiB apart, each nb bytes
+    assert all(v.numel() == nb for v in views)
+    keep_busy(lambda i: bsk.debug_stream_read(views[i % 3], sink, best_grid, stream), 0.05)
+    e0.record(stream)
+    for i in range(reps * 3):
+        bsk.debug_stream_read(views[i % 3], sink, best_grid, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / (reps * 3)
+    out["read_decode_volume_us"] = round(s * 1e6, 1)
+    out["read_decode_volume_gbs"] = round(nb / s / 1e9, 1)
+    out["note"] = ("GEMM: 2 n^3 flop per torch.matmul, n = 8192; copy: 2 GiB read + 2 GiB written per copy; "
+                   "read: bsk_debug_stream_read over 2 GiB, best of 4/8/16 workgroups per CU, and over the Llama-3 "
+                   "decode's 695.8 MB per launch")
+    del src
     return out
 
 

@@ -78,6 +78,7 @@ _sig = {
     "bsk_run_noalloc": [P(Problem), P(PlanInfo), P(Tensors), vp, vp],
     "bsk_rope_table": [vp, i32, i32, f64, vp],
     "bsk_debug_gather": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp, vp, vp],
+    "bsk_debug_stream_read": [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, vp],
     "bsk_rope_apply": [P(Problem), i32, i32, vp, vp, vp, P(Tensors), vp, i64, i64, vp, vp],
     "bsk_append_paged_kv": [P(Problem), i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64,
                             i64, vp],
@@ -210,6 +211,12 @@ def debug_gather(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, row
                  stream=None):
     _ok(_lib.bsk_debug_gather(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
                               _ptr(row_offsets), _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def debug_stream_read(src, sink, grid: int, stream=None):
+    """Measurement hook: read all of src (a device buffer) once; sink receives one XOR word per
+    thread."""
+    _ok(_lib.bsk_debug_stream_read(_ptr(src), _nbytes(src), _ptr(sink), _nbytes(sink), int(grid), _stream(stream)))
 
 
 EXPORTED = ["bsk_status_string", "bsk_last_error", *_sig.keys()]

@@ -640,5 +640,18 @@ bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* inf
   return BSK_OK;
 }
 
+bsk_status bsk_debug_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, int32_t grid,
+                                 void* stream) {
+  if (!src || !sink) return fail(BSK_ERR_INVALID_ARG, "null argument");
+  if (!aligned(src, 16) || bytes % 16 != 0) return fail(BSK_ERR_INVALID_ARG, "src must be 16-byte aligned, bytes a multiple of 16");
+  if (grid <= 0 || grid > (1 << 20)) return fail(BSK_ERR_INVALID_ARG, "grid must be in [1, 2^20]");
+  if (!aligned(sink, 4) || sink_bytes < size_t(grid) * size_t(bsk::stream_read_threads()) * sizeof(uint32_t))
+    return fail(BSK_ERR_INVALID_ARG, "sink must hold one 32-bit word per thread (grid * 256)");
+  hipError_t e = bsk::launch_stream_read(src, int64_t(bytes / 16), static_cast<uint32_t*>(sink), grid,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return BSK_OK;
+}
+
 }  // extern "C"
 #pragma GCC visibility pop

@@ -1,4 +1,5 @@
-// Partial-state merge, plan upload, RoPE table and the gather test hook.
+// Partial-state merge, plan upload, RoPE table, the gather test hook and a streaming-read
+// measurement hook.
 //
 // Split-KV (FlashInfer 0.6 wiki, "Kernel types": the split_kv decode path)
 // leaves one (O_c, LSE_c) per key chunk; the exact combination is
@@ -135,7 +136,42 @@ __global__ __launch_bounds__(256) void plan_upload_kernel(const uint32_t* __rest
   }
 }
 
+// Streaming read (a measurement hook, not part of the method): every 16-byte piece of the buffer
+// is loaded exactly once, four independent loads per thread in flight, non-temporal (the data is
+// not reused).  Each thread stores the XOR of the words it read, so the XOR over all stores is the
+// XOR of the buffer's words: the caller can check that every byte was read.
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 4;
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                                    uint32_t* __restrict__ sink) {
+  const int64_t tid = int64_t(blockIdx.x) * kReadThreads + threadIdx.x;
+  const int64_t stride = int64_t(gridDim.x) * kReadThreads;
+  uint32_t x = 0;
+  int64_t i = tid;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  sink[tid] = x;
+}
+
 // ---------------------------------------------------------------- host launchers
+
+int stream_read_threads() { return kReadThreads; }
+
+hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kReadThreads), 0, stream, static_cast<const u32x4*>(src),
+                     n16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan_upload(const void* src_dev, void* dst, int64_t words, hipStream_t stream) {
   const int64_t grid = (words + 1023) / 1024;

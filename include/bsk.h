@@ -409,6 +409,20 @@ bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* inf
                             const void* int_ws_dev, const int64_t* row_offsets, void* k_out, void* v_out,
                             void* stream);
 
+/*
+ * Measurement hook, not part of the method: the device's practical rate for
+ * a plain streaming read, the ceiling an HBM-bound kernel such as the decode
+ * is compared with.  Reads bytes of src (device memory, 16-byte aligned,
+ * bytes a multiple of 16) once, with `grid` workgroups of 256 threads and
+ * 16-byte non-temporal loads, and writes one 32-bit word per thread into
+ * sink (grid * 256 words, caller-owned): the XOR of the words that thread
+ * read, so that the XOR of all of sink equals the XOR of all of src.
+ * Errors: INVALID_ARG (null or misaligned pointers, grid outside
+ * [1, 2^20], sink too small), HIP.
+ */
+bsk_status bsk_debug_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, int32_t grid,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

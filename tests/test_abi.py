@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(bsk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -151,3 +151,14 @@ def test_one_hip_runtime_in_the_process():
     with open("/proc/self/maps") as f:
         mapped = {line.split()[-1] for line in f if "amdhip64" in line}
     assert len(mapped) == 1, mapped
+
+
+def test_stream_read_rejects_bad_arguments():
+    import ctypes as C
+    f = bsk._lib.bsk_debug_stream_read
+    assert f(None, 1024, 0x10000, 1 << 20, 8, None) == bsk.ERR_INVALID_ARG
+    assert f(0x10008, 1024, 0x10000, 1 << 20, 8, None) == bsk.ERR_INVALID_ARG   # src not 16-byte aligned
+    assert f(0x10000, 1000, 0x20000, 1 << 20, 8, None) == bsk.ERR_INVALID_ARG   # bytes not a multiple of 16
+    assert f(0x10000, 1024, 0x20000, 8 * 256 * 4 - 4, 8, None) == bsk.ERR_INVALID_ARG  # sink too small
+    assert f(0x10000, 1024, 0x20000, 1 << 20, 0, None) == bsk.ERR_INVALID_ARG   # empty grid
+    assert "grid" in bsk.last_error()
