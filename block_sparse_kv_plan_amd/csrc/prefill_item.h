@@ -342,34 +342,31 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
         logits(0, st2[0]);
         logits(1, st2[1]);
       }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if constexpr (LIVE == 1) logits(ks, st2[0]);
-        f32x4 (&st)[2][NB] = st2[LIVE == 2 ? ks : 0];
-        if (!clean) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const RowMask rm = row_mask(row_ok[nb], qpos[nb], kv_hi, a.causal, a.window, a.sink);
-#pragma unroll
-            for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                st[mh][nb][i] = row_sees(rm, kt + 16 * (2 * ks + mh) + 4 * j + i) ? st[mh][nb][i] : -INFINITY;
-          }
-        }
-        // Online softmax with a lazily moved reference: each lane checks its own logits against
-        // the row's threshold; only if some lane exceeds it is the row max reduced across the
-        // row's four lanes and the state rescaled.
-        float lmax[NB];
-        uint64_t grow = 0;
+      // masks of half ks, only where the tile crosses a boundary for some row of this wave
+      auto mask_half = [&](f32x4 (&st)[2][NB], int ks) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          float x = fmaxf(fmaxf(st[0][nb][0], st[0][nb][1]), st[0][nb][2]);
-          x = fmaxf(fmaxf(x, st[0][nb][3]), st[1][nb][0]);
-          x = fmaxf(fmaxf(x, st[1][nb][1]), st[1][nb][2]);
-          lmax[nb] = fmaxf(x, st[1][nb][3]);
-          grow |= __builtin_amdgcn_ballot_w64(lmax[nb] > thr[nb]);
+          const RowMask rm = row_mask(row_ok[nb], qpos[nb], kv_hi, a.causal, a.window, a.sink);
+#pragma unroll
+          for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              st[mh][nb][i] = row_sees(rm, kt + 16 * (2 * ks + mh) + 4 * j + i) ? st[mh][nb][i] : -INFINITY;
         }
+      };
+      auto half_max = [&](const f32x4 (&st)[2][NB], int nb) {
+        float x = fmaxf(fmaxf(st[0][nb][0], st[0][nb][1]), st[0][nb][2]);
+        x = fmaxf(fmaxf(x, st[0][nb][3]), st[1][nb][0]);
+        x = fmaxf(fmaxf(x, st[1][nb][1]), st[1][nb][2]);
+        return fmaxf(x, st[1][nb][3]);
+      };
+      // Online softmax with a lazily moved reference: each lane checks its own logits against
+      // the row's threshold; only if some lane exceeds it is the row max reduced across the
+      // row's four lanes and the state rescaled.
+      auto maybe_rescale = [&](const float (&lmax)[NB]) {
+        uint64_t grow = 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) grow |= __builtin_amdgcn_ballot_w64(lmax[nb] > thr[nb]);
         if (grow) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
@@ -385,8 +382,9 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
             }
           }
         }
-        // P (bf16 operand of the PV product) and the row sums
-        bf16x8 pb[NB];
+      };
+      // P of a half (bf16 operand of the PV product) and the row sums
+      auto probs = [&](const f32x4 (&st)[2][NB], bf16x8 (&pb)[NB]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           u32x4 pw;
@@ -404,28 +402,61 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
           // the row sum adds the fp32 values: the log-sum-exp keeps their precision
           l_run[nb] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
         }
-
-        // O^T[d][row] += V^T P^T.  MFMA k index 8j+e <-> key 32ks + 4j + (e&3) + 16(e>>2): the
-        // keys whose probabilities this lane holds.  The V^T operand comes from two transposing
-        // LDS reads: in each 16-lane group, lane k points at 4 columns of key row k/4 and gets
-        // back one column of 4 keys, so lane (n, j) receives V[key(8j+e)][16 db + n].
-        {
-          const unsigned short* vb = sv + (32 * ks + v_row) * D + v_half;
-          constexpr int VB = NB <= 2 ? NDB : 2;  // V^T operands read ahead of their MFMAs
+      };
+      // O^T[d][row] += V^T P^T for half ks.  MFMA k index 8j+e <-> key 32ks + 4j + (e&3) + 16(e>>2):
+      // the keys whose probabilities this lane holds.  The V^T operand comes from two transposing
+      // LDS reads: in each 16-lane group, lane k points at 4 columns of key row k/4 and gets back
+      // one column of 4 keys, so lane (n, j) receives V[key(8j+e)][16 db + n].
+      auto pv = [&](const bf16x8 (&pb)[NB], int ks) {
+        const unsigned short* vb = sv + (32 * ks + v_row) * D + v_half;
+        constexpr int VB = NB <= 2 ? NDB : 2;  // V^T operands read ahead of their MFMAs
 #pragma unroll
-          for (int d0 = 0; d0 < NDB; d0 += VB) {
-            bf16x8 va[VB];
+        for (int d0 = 0; d0 < NDB; d0 += VB) {
+          bf16x8 va[VB];
 #pragma unroll
-            for (int i = 0; i < VB; ++i) {
-              const int off = 8 * ((2 * (d0 + i) + ((n & 3) >> 1)) ^ v_sw);
-              va[i] = ds_read_tr_pair(vb + off, vb + off + 16 * D);
-            }
-#pragma unroll
-            for (int i = 0; i < VB; ++i)
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                acc[nb][d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pb[nb], acc[nb][d0 + i], 0, 0, 0);
+          for (int i = 0; i < VB; ++i) {
+            const int off = 8 * ((2 * (d0 + i) + ((n & 3) >> 1)) ^ v_sw);
+            va[i] = ds_read_tr_pair(vb + off, vb + off + 16 * D);
           }
+#pragma unroll
+          for (int i = 0; i < VB; ++i)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[nb][d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pb[nb], acc[nb][d0 + i], 0, 0, 0);
+        }
+      };
+
+      if constexpr (LIVE == 2) {
+        // Both halves' logits are in registers: the reference moves at most once per tile (from
+        // the maximum over both halves), so no branch separates half 1's exponentials from half
+        // 0's PV products, and the matrix cores run those products while the exponentials go
+        // through the transcendental unit.
+        if (!clean) {
+          mask_half(st2[0], 0);
+          mask_half(st2[1], 1);
+        }
+        float lmax[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) lmax[nb] = fmaxf(half_max(st2[0], nb), half_max(st2[1], nb));
+        maybe_rescale(lmax);
+        bf16x8 p0[NB], p1[NB];
+        probs(st2[0], p0);
+        pv(p0, 0);
+        probs(st2[1], p1);
+        pv(p1, 1);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          logits(ks, st2[0]);
+          f32x4 (&st)[2][NB] = st2[0];
+          if (!clean) mask_half(st, ks);
+          float lmax[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) lmax[nb] = half_max(st, nb);
+          maybe_rescale(lmax);
+          bf16x8 pb[NB];
+          probs(st, pb);
+          pv(pb, ks);
         }
       }
     };
