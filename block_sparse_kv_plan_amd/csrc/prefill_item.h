@@ -342,16 +342,32 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
         logits(0, st2[0]);
         logits(1, st2[1]);
       }
-      // masks of half ks, only where the tile crosses a boundary for some row of this wave
+      // masks of half ks, only where the tile crosses a boundary for some row of this wave.  The
+      // lane's keys are base + 16 mh + i, so without a window a key is visible iff its constant
+      // offset is below the row's bound minus base: one compare with an immediate per key.
       auto mask_half = [&](f32x4 (&st)[2][NB], int ks) {
+        const int base = kt + 32 * ks + 4 * j;
+        if (a.window > 0) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const RowMask rm = row_mask(row_ok[nb], qpos[nb], kv_hi, a.causal, a.window, a.sink);
+          for (int nb = 0; nb < NB; ++nb) {
+            const RowMask rm = row_mask(row_ok[nb], qpos[nb], kv_hi, a.causal, a.window, a.sink);
 #pragma unroll
-          for (int mh = 0; mh < 2; ++mh)
+            for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              st[mh][nb][i] = row_sees(rm, kt + 16 * (2 * ks + mh) + 4 * j + i) ? st[mh][nb][i] : -INFINITY;
+              for (int i = 0; i < 4; ++i)
+                st[mh][nb][i] = row_sees(rm, base + 16 * mh + i) ? st[mh][nb][i] : -INFINITY;
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            // keys [.., hi) are visible: the range end and, if causal, the row's position
+            const int hi = a.causal ? min(kv_hi, qpos[nb] + 1) : kv_hi;
+            const int lim = row_ok[nb] ? hi - base : 0;  // offsets below lim are visible
+#pragma unroll
+            for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) st[mh][nb][i] = 16 * mh + i < lim ? st[mh][nb][i] : -INFINITY;
+          }
         }
       };
       auto half_max = [&](const f32x4 (&st)[2][NB], int nb) {
