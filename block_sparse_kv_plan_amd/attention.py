@@ -160,6 +160,10 @@ class BatchAttention:
         self.float_ws = torch.empty(max(float_b, 16), dtype=torch.uint8, device=self.device)
         self.host_ws = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
         self.info: Optional[PlanInfo] = None
+        self._init_order()
+
+    def _init_order(self):
+        """The events and streams that order reuse of the workspaces (host and device)."""
         self._uploaded = torch.cuda.Event()   # the plan copy out of host_ws has completed (recorded lazily)
         self._consumed = _HostOrderEvent()    # the last run reading int_ws has completed
         self._merged = _HostOrderEvent()      # the last merge reading int_ws / float_ws has completed
@@ -170,10 +174,13 @@ class BatchAttention:
         self._upload_stream = None
         # An event recorded on the kernels' queue costs GPU time (it ends in a release the host can
         # see), so the upload gets one only when something needs it: a run on another stream, or
-        # the next plan when no merge on the upload's own stream (whose event comes later in that
-        # stream) has been recorded since.
+        # the next plan when no run of this plan has been merged or settled since.  Every run waits
+        # for its plan's upload, so the event of its merge (or its own, when the merge is fused or
+        # never called) completes after the upload too, and the next plan waits for that instead:
+        # an upload event recorded only then would sit behind all the work queued meanwhile.
         self._upload_recorded = False
-        self._upload_covered = False
+        self._ran = False          # a run (or replay) of the last plan has been launched
+        self._upload_cover = None  # an event recorded after such a run, hence after the upload
 
     @classmethod
     def create(cls, *, device="cuda", num_workers=None, **kw):
@@ -186,36 +193,48 @@ class BatchAttention:
             self._uploaded.record(self._upload_stream)
             self._upload_recorded = True
 
+    def _recorded(self, ev):
+        """Note that `ev` has just been recorded after a run of the last plan (a run waits for its
+        plan's upload, and a merge on another stream waits for the run), so it completes after
+        the upload."""
+        if self._upload_pending and self._ran:
+            self._upload_cover = ev
+
     def plan(self, qo_indptr, kv_len, kv_indptr, stream=None, copy_stream=None) -> PlanInfo:
+        self._settle_run()
+        synced = None
         if self._upload_pending:  # host_ws may still be read by the previous upload
-            if self._upload_covered:
-                self._merged.synchronize()  # recorded after it on the same stream
+            if self._upload_cover is not None:
+                synced = self._upload_cover
             else:
                 self._record_upload()
-                self._uploaded.synchronize()
+                synced = self._uploaded
+            synced.synchronize()
         stream = stream or torch.cuda.current_stream(self.device)
         up = copy_stream if copy_stream is not None else stream
-        self._settle_run()
         # Do not overwrite int_ws under a kernel that still reads it on another stream: wait for the
         # last run and the last merge (one wait when both went to the same stream, the merge last).
         # The wait is on the host.  A GPU-side wait queued in front of the upload made every copy
         # behind it cost ~50 us of host time in the runtime, and once per process stalled one copy
         # for several milliseconds; with two or more workspaces in turn the last run on this one
         # has normally finished by the time it is planned again, so the host wait returns at once.
+        # (a torch stream compares unequal to nothing, None included: `stream != None` is False)
         waits = []
         if self._merged_stream is not None:
             waits.append((self._merged, self._merged_stream))
-        if self._consumed_stream is not None and self._consumed_stream != self._merged_stream:
+        if self._consumed_stream is not None and (self._merged_stream is None
+                                                  or self._consumed_stream != self._merged_stream):
             waits.append((self._consumed, self._consumed_stream))
         for ev, st in waits:
-            if st != up:
+            if st != up and ev is not synced:
                 ev.synchronize()
         self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
                          self.host_ws, self.int_ws, up)
         self._upload_pending = True
         self._upload_stream = up
         self._upload_recorded = False
-        self._upload_covered = False
+        self._ran = False
+        self._upload_cover = None
         return self.info
 
     def run(self, tensors: Tensors, stream=None, merge: bool = True, wait_upload: bool = True):
@@ -230,6 +249,7 @@ class BatchAttention:
             run_decode(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         else:
             run_prefill(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        self._ran = True
         self._consumed_stream = None
         self._merged_stream = None  # the last merge event belongs to an earlier run
         # The merge that follows (on this stream, or on one the caller made wait for this run) ends
@@ -244,6 +264,7 @@ class BatchAttention:
         everything queued on the run's stream so far)."""
         if self._run_stream is not None:
             self._consumed.record(self._run_stream)
+            self._recorded(self._consumed)
             self._consumed_stream = self._run_stream
             self._run_stream = None
 
@@ -275,9 +296,10 @@ class BatchAttention:
             stream.wait_event(self._uploaded)
         with torch.cuda.stream(stream):
             graph.replay()
+        self._ran = True
         self._merged.record(stream)
+        self._recorded(self._merged)
         self._merged_stream = stream
-        self._upload_covered = self._upload_pending and self._upload_stream == stream
         self._consumed_stream = None
         self._run_stream = None
 
@@ -290,8 +312,8 @@ class BatchAttention:
         stream = stream or torch.cuda.current_stream(self.device)
         merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
         self._merged.record(stream)
+        self._recorded(self._merged)
         self._merged_stream = stream
-        self._upload_covered = self._upload_pending and self._upload_stream == stream
         self._run_stream = None
 
 

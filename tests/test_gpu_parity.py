@@ -345,19 +345,23 @@ def test_rope_head_dim_64():
 
 # ------------------------------------------------------------------ plan upload on a copy stream
 
-def test_copy_stream_uploads_alternating_plans():
+@pytest.mark.parametrize("fused", [0, 1])
+def test_copy_stream_uploads_alternating_plans(fused):
     """Two plan workspaces used alternately, a different batch (lengths, hence plan) every step,
     each plan uploaded on a side stream while the main stream still runs earlier steps, and the
-    merges on a third stream: every step's output equals the same step run in one stream, bit for
-    bit, and the oracle."""
+    merges on a third stream (or merged in the kernel): every step's output equals the same step
+    run in one stream, bit for bit, and the oracle.  The main stream is kept busy first, so every
+    plan is made while the runs before it are still queued: a plan that did not wait for the last
+    run reading its workspace would overwrite that run's plan."""
     dev = require_gpu()
     Hq, Hk, d = 32, 8, 128
     rng = np.random.default_rng(83)
     batches = [small(83 + i, rng.integers(1, 3000, size=int(rng.integers(3, 12))), Hq=Hq, Hk=Hk, d=d, causal=True)
                for i in range(6)]
-    say("copy-stream plan uploads over 6 steps")
+    say(f"copy-stream plan uploads over 6 steps, fused merge {fused}")
     attn = [BatchAttention.create(device=dev, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=d, dtype=bsk.DTYPE_BF16,
-                                  causal=True, max_batch=16) for _ in range(2)]
+                                  causal=True, max_batch=16, fused_merge=fused) for _ in range(2)]
+    busy = torch.randn((4096, 4096), dtype=torch.float32, device=dev)
     dus = [upload(bb) for bb in batches]
     side = torch.cuda.Stream()
     main = torch.cuda.current_stream()
@@ -373,6 +377,8 @@ def test_copy_stream_uploads_alternating_plans():
     for copy_stream, merge_stream in ((None, None), (side, None), (side, merge_side)):
         outs = outputs()
         torch.cuda.synchronize()
+        for _ in range(8):  # ~10 ms of queued work ahead of the first run
+            busy = busy @ busy * (1.0 / 64.0)
         for i, (bb, du) in enumerate(zip(batches, dus)):
             a = attn[i % 2]
             t = tensors_for(a.problem, du["q"], du["k"], du["v"], outs[i][0], outs[i][1], page_indices=du["pages"])
