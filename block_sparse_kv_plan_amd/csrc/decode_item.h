@@ -253,23 +253,27 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
       // so the V loads carry the non-temporal hint and their lines do not linger in L2.  A K load
       // covers half of each line it touches (four 16-byte pieces of a key row); the hint on K
       // measured slower (a streamed line may leave L2 before its other half is read).
-      auto load_block = [&](int b, bf16x8* kf, u32x4* vf) {
+      // A wave past its last block still issues a block's loads (`dummy`), so that every iteration
+      // issues the same loads.  With a block inside one page they all read the block's first key
+      // row (512 B of K and V instead of the block's 8 KB: on short items, where the block has
+      // already left L2, re-reading it whole cost up to an eighth more traffic).
+      auto load_block = [&](int b, bf16x8* kf, u32x4* vf, bool dummy) {
         const int tb = (blk0 + b) << 4;
         if (block_in_page) {
           const int t0 = min(max(tb, kmin), kmax);
           int64_t kb, vb;
           key_offsets(t0, kb, vb);  // one page id serves the whole block
-          const int tk = min(max(tb + kkey, kmin), kmax);
+          const int tk = dummy ? t0 : min(max(tb + kkey, kmin), kmax);
 #pragma unroll
           for (int s = 0; s < NKS; ++s)
             kf[s] = *reinterpret_cast<const bf16x8*>(Kp + kb + int64_t(tk - t0) * a.k_st + 8 * (4 * s + j));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tv = min(max(tb + 4 * i + j, kmin), kmax);
+            const int tv = dummy ? t0 : min(max(tb + 4 * i + j, kmin), kmax);
             vf[i] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4*>(Vp + vb + int64_t(tv - t0) * a.v_st + 8 * (n % CHUNKS)));
           }
-        } else {
+        } else {  // pages of < 16 keys: a dummy block is read whole (its rows may span pages)
           int64_t ko, vo;
           key_offsets(min(max(tb + kkey, kmin), kmax), ko, vo);
 #pragma unroll
@@ -372,7 +376,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 
       // Two register sets: the next block's loads are in flight while the current one is consumed.
       // Every iteration issues the same loads in the same order -- a wave without a next block
-      // reads its current block again (an L2 hit) -- so the wait before a block's math only has
+      // issues dummy loads from its current block -- so the wait before a block's math only has
       // to let the next block's loads (and, with RoPE, nothing else) stay outstanding; a load
       // skipped on some path would force a wait for everything issued so far.  The RoPE table
       // values of a block are requested before the next block's K/V for the same reason.
@@ -380,16 +384,16 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
       u32x4 va[4], vb2[4];
       float4 cs[NCS];
       int b = wave_u;
-      if (b < nblk) load_block(b, ka, va);
+      if (b < nblk) load_block(b, ka, va, false);
       for (; b < nblk; b += 2 * kDecWaves) {
         const int b1 = b + kDecWaves;
         next_table(b, cs);
-        load_block(b1 < nblk ? b1 : b, kb2, vb2);
+        load_block(b1 < nblk ? b1 : b, kb2, vb2, b1 >= nblk);
         compute_block(b, ka, va, cs);
         if (b1 >= nblk) break;
         const int b2 = b1 + kDecWaves;
         next_table(b1, cs);
-        load_block(b2 < nblk ? b2 : b1, ka, va);
+        load_block(b2 < nblk ? b2 : b1, ka, va, b2 >= nblk);
         compute_block(b1, kb2, vb2, cs);
       }
     } else {
