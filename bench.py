@@ -97,8 +97,10 @@ def make_attention(batch, tile_q, out_dtype, device, **kw):
 class Runner:
     """Device copies of one batch plus two alternating plan workspaces.  upload="stream" (default)
     uploads each step's plan on the kernels' own stream; upload="copy" puts it on a copy stream that
-    the kernels wait for.  On the Llama-3 decode the in-stream upload measured ~0.7 us per step
-    faster (no cross-stream wait, which also costs ~13 us of host time)."""
+    the kernels wait for (on the Llama-3 decode ~0.7 us per step slower: a cross-stream wait, which
+    also costs ~13 us of host time); upload="merge" defers each plan's upload into the launch of
+    the previous step's merge (bsk_merge_states_upload), so a step is plan, run, and the merge of
+    the previous step carrying this step's upload; flush() then merges the last run."""
 
     def __init__(self, batch, tile_q, copies, device, out_dtype=0, graphs=False, upload="stream", **plan_kw):
         import torch
@@ -107,8 +109,11 @@ class Runner:
         from block_sparse_kv_plan_amd.attention import tensors_for
         from workloads.device import rope_positions_needed
         from workloads.device import upload as upload_batch
-        if upload not in ("copy", "stream"):
-            raise ValueError(f"upload must be 'copy' or 'stream', not {upload!r}")
+        if upload not in ("copy", "stream", "merge"):
+            raise ValueError(f"upload must be 'copy', 'stream' or 'merge', not {upload!r}")
+        if upload == "merge" and graphs:
+            raise ValueError("graph replay holds the run and its merge; upload='merge' merges separately")
+        self._pending = None  # (workspace, tensors) of a run whose merge is still to come
         self.batch = batch
         self.upload = upload
         self.attn = [make_attention(batch, tile_q, out_dtype, device, **plan_kw) for _ in range(2)]
@@ -149,12 +154,27 @@ class Runner:
         """One pass of the hot path: host plan + upload (on the copy stream when given), the
         attention kernel, then the split-KV state merge (replayed from a graph when captured)."""
         a = self.attn[i % 2]
-        a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, copy_stream=copy_stream)
         c = i % len(self.tensors)
+        if self.upload == "merge":
+            a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, defer_upload=True)
+            if self._pending is not None:
+                self._pending[0].merge(self._pending[1], stream, upload_next=a)
+            else:
+                a.upload(stream)
+            a.run(self.tensors[c], stream=stream, merge=False)
+            self._pending = (a, self.tensors[c])
+            return
+        a.plan(self.batch.qo_indptr, self.batch.kv_len, self.kv_indptr, stream=stream, copy_stream=copy_stream)
         if self.graphs is not None:
             a.replay(self.graphs[(i % 2, c)], stream)
         else:
             a.run(self.tensors[c], stream=stream)
+
+    def flush(self, stream):
+        """The merge still owed by the last step (upload="merge"); nothing otherwise."""
+        if self._pending is not None:
+            self._pending[0].merge(self._pending[1], stream)
+            self._pending = None
 
 
 WARM_S = 0.25  # sustained load before a secondary leg's timing (MFMA-bound kernels run ~20% slower for
@@ -204,12 +224,14 @@ def wall_clock(runner, steps, warmup, warm_s=0.0):
             one(i)
         if warm_s > 0:
             keep_busy(one, warm_s)
+        runner.flush(stream)
         torch.cuda.synchronize()
         first = done[0]
         t0 = time.perf_counter()
         for i in range(steps):
             runner.step(first + i, stream, copy_stream=copy_stream)
             stamps[i] = time.perf_counter()
+        runner.flush(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     finally:
@@ -516,9 +538,9 @@ def main():
     ap.add_argument("--graph", type=int, choices=(0, 1), default=0,
                     help="replay each step's run + merge from a graph captured at set-up (1) or launch them "
                          "directly (0, default: two direct launches measured faster than one graph launch)")
-    ap.add_argument("--upload", choices=("copy", "stream"), default="stream",
-                    help="where the Llama-3 decode leg uploads each plan: on the kernels' own stream (default) or "
-                         "on a copy stream the kernels wait for")
+    ap.add_argument("--upload", choices=("copy", "stream", "merge"), default="merge",
+                    help="where the Llama-3 decode leg uploads each plan: in the previous step's merge launch "
+                         "(default), on the kernels' own stream, or on a copy stream the kernels wait for")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
@@ -557,8 +579,9 @@ def main():
         dkw = {k: v for k, v in (("split_factor", args.decode_split), ("min_chunk", args.decode_min_chunk),
                                   ("item_overhead", args.decode_overhead), ("fused_merge", args.fused_merge))
                if v is not None}
-        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device, graphs=bool(args.graph), upload=args.upload,
-                        **dkw)
+        # a replayed graph holds the run and its merge, so it uploads in-stream instead of in the merge
+        up_mode = "stream" if args.graph and args.upload == "merge" else args.upload
+        runner = Runner(b, bsk.TILE_DECODE, copies=4, device=device, graphs=bool(args.graph), upload=up_mode, **dkw)
         log(f"decode: {int(b.kv_len.sum())} keys, {nbytes / 1e9:.3f} GB per step; timing {args.steps} steps")
         m = wall_clock(runner, args.steps, args.warmup)
         m.update(kernel_durations(runner, max(20, min(args.steps, 100))))
@@ -566,7 +589,10 @@ def main():
         achieved = nbytes / m["kernel_s_mean"] / 1e9
         plan_us = plan_host_us(runner)
         traffic = load_traffic("decode_llama3", nbytes)
-        where_up = "on a copy stream" if args.upload == "copy" else "on the kernels' stream"
+        step_desc = {"copy": "plan + upload on a copy stream + run + merge",
+                     "stream": "plan + upload on the kernels' stream + run + merge",
+                     "merge": "plan + run + merge, each plan's upload made in the launch of the previous step's "
+                              "merge; the first upload and the last merge on their own"}[up_mode]
         result = {
             "metric": "paged decode HBM TB/s (% of 8 TB/s peak); ragged prefill TFLOPS (% MFMA peak)",
             "value": round(nbytes / m["wall_s"] / 1e12, 4),
@@ -588,7 +614,7 @@ def main():
                        "plan_imbalance": round(info.max_load / max(1.0, info.total_cost / info.num_workers), 3),
                        "plan_host_us": plan_us, "graph_replay": bool(args.graph),
                        "parallelism": "single GPU"},
-            "timing": {"protocol": f"wall clock over the timed steps (plan + upload {where_up} + run + merge, "
+            "timing": {"protocol": f"wall clock over the timed steps ({step_desc}; "
                                    "no events in the loop, garbage collector paused); kernel durations from HIP "
                                    "events around the kernel in a separate pass afterwards",
                        "host_submit_us_median": m["host_submit_us_median"],

@@ -73,7 +73,10 @@ _sig = {
     "bsk_plan": [P(Problem), i32, vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, P(PlanInfo)],
     "bsk_run_decode": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
     "bsk_run_prefill": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
+    "bsk_upload_plan": [P(Problem), P(PlanInfo), vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp],
     "bsk_merge_states": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, vp],
+    "bsk_merge_states_upload": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, ctypes.c_size_t, P(Problem), P(PlanInfo),
+                                vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp],
     "bsk_merge_state_pair": [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp],
     "bsk_run_noalloc": [P(Problem), P(PlanInfo), P(Tensors), vp, vp],
     "bsk_rope_table": [vp, i32, i32, f64, vp],
@@ -160,6 +163,12 @@ def plan(problem: Problem, qo_indptr, kv_len, kv_indptr, host_ws, int_ws=None, s
     return info
 
 
+def upload_plan(problem: Problem, info: PlanInfo, host_ws, int_ws, stream=None):
+    """Copy a plan built on the host only (plan() without int_ws) into the int workspace."""
+    _ok(_lib.bsk_upload_plan(ctypes.byref(problem), ctypes.byref(info), _ptr(host_ws), _nbytes(host_ws),
+                             _ptr(int_ws), _nbytes(int_ws), _stream(stream)))
+
+
 def run_decode(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, float_ws, stream=None):
     _ok(_lib.bsk_run_decode(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
                             _ptr(float_ws), 0 if float_ws is None else _nbytes(float_ws), _stream(stream)))
@@ -173,6 +182,16 @@ def run_prefill(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, floa
 def merge_states(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, float_ws, stream=None):
     _ok(_lib.bsk_merge_states(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
                               _ptr(float_ws), 0 if float_ws is None else _nbytes(float_ws), _stream(stream)))
+
+
+def merge_states_upload(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, float_ws, next_problem: Problem,
+                        next_info: PlanInfo, next_host_ws, next_int_ws, stream=None):
+    """merge_states of one run and upload_plan of the next plan (another int workspace), one launch."""
+    _ok(_lib.bsk_merge_states_upload(ctypes.byref(problem), ctypes.byref(info), ctypes.byref(tensors), _ptr(int_ws),
+                                     _ptr(float_ws), 0 if float_ws is None else _nbytes(float_ws),
+                                     ctypes.byref(next_problem), ctypes.byref(next_info), _ptr(next_host_ws),
+                                     _nbytes(next_host_ws), _ptr(next_int_ws), _nbytes(next_int_ws),
+                                     _stream(stream)))
 
 
 def run_noalloc(problem: Problem, info: PlanInfo, tensors: Tensors, int_ws, stream=None):

@@ -13,8 +13,8 @@ import numpy as np
 import torch
 
 from . import (DTYPE_BF16, DTYPE_F32, KV_DENSE, KV_PAGED, ROPE_NONE, TILE_DECODE, TILE_PREFILL, TILE_PREFILL_256, PlanInfo,
-               Problem, Tensors, append_paged_kv, device_workers, merge_state_pair, merge_states, plan, run_decode,
-               run_prefill, workspace_query)
+               Problem, Tensors, append_paged_kv, device_workers, merge_state_pair, merge_states, merge_states_upload,
+               plan, run_decode, run_prefill, upload_plan, workspace_query)
 
 TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
 
@@ -150,7 +150,9 @@ class BatchAttention:
     The plan upload can go on its own copy stream, and the merge can run on a stream of its own
     (merge()): plan() first waits (on the host) for the last run and the last merge that read this
     workspace on other streams, and run() waits (on the GPU) for the upload, so a host plan, its
-    copy and the previous step's merge overlap the GPU work already queued."""
+    copy and the previous step's merge overlap the GPU work already queued.  With two workspaces in
+    turn, plan(defer_upload=True) leaves the upload to the other workspace's merge
+    (merge(..., upload_next=...)), which then makes it in the same launch."""
 
     def __init__(self, problem: Problem, device="cuda"):
         self.problem = problem
@@ -181,6 +183,7 @@ class BatchAttention:
         self._upload_recorded = False
         self._ran = False          # a run (or replay) of the last plan has been launched
         self._upload_cover = None  # an event recorded after such a run, hence after the upload
+        self._deferred = None      # the stream a deferred upload of the last plan must go to
 
     @classmethod
     def create(cls, *, device="cuda", num_workers=None, **kw):
@@ -200,7 +203,11 @@ class BatchAttention:
         if self._upload_pending and self._ran:
             self._upload_cover = ev
 
-    def plan(self, qo_indptr, kv_len, kv_indptr, stream=None, copy_stream=None) -> PlanInfo:
+    def plan(self, qo_indptr, kv_len, kv_indptr, stream=None, copy_stream=None, defer_upload=False) -> PlanInfo:
+        """Plan the step on the host and upload it (on copy_stream if given, else on `stream`).  With
+        defer_upload the upload is left to upload() or to another workspace's merge(upload_next=...),
+        on that same stream; until then run() refuses to start."""
+        self._deferred = None  # a deferred upload not made yet is superseded: nothing of it is queued
         self._settle_run()
         synced = None
         if self._upload_pending:  # host_ws may still be read by the previous upload
@@ -228,19 +235,52 @@ class BatchAttention:
         for ev, st in waits:
             if st != up and ev is not synced:
                 ev.synchronize()
+        if defer_upload:
+            self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
+                             self.host_ws)
+            self._upload_pending = False  # nothing queued reads host_ws until the upload is made
+            self._deferred = up
+            self._ran = False
+            self._upload_cover = None
+            return self.info
         self.info = plan(self.problem, np.asarray(qo_indptr), np.asarray(kv_len), np.asarray(kv_indptr),
                          self.host_ws, self.int_ws, up)
+        self._uploaded_on(up)
+        return self.info
+
+    def _uploaded_on(self, stream):
+        """The last plan's upload has just been enqueued on `stream`."""
+        self._deferred = None
         self._upload_pending = True
-        self._upload_stream = up
+        self._upload_stream = stream
         self._upload_recorded = False
         self._ran = False
         self._upload_cover = None
-        return self.info
+
+    def _deferred_stream(self, stream):
+        if self._deferred is None:
+            raise RuntimeError("no deferred upload: plan(..., defer_upload=True) first")
+        stream = stream or self._deferred
+        if stream != self._deferred:
+            raise ValueError("a deferred upload goes to the stream its plan named (its reuse waits were taken for it)")
+        return stream
+
+    def upload(self, stream=None):
+        """Make the deferred upload of the last plan on `stream` (the stream the plan named)."""
+        stream = self._deferred_stream(stream)
+        upload_plan(self.problem, self.info, self.host_ws, self.int_ws, stream)
+        self._uploaded_on(stream)
+
+    def _refuse_deferred(self):
+        if self._deferred is not None:
+            raise RuntimeError("the last plan's upload is deferred: upload() it, or merge another workspace's run "
+                               "with upload_next=this workspace, first")
 
     def run(self, tensors: Tensors, stream=None, merge: bool = True, wait_upload: bool = True):
         """Attention (and, unless merge is False, the merge) for the last plan.  A plan uploaded on
         another stream is waited for on `stream` first; wait_upload=False leaves that wait to the
         caller (who must have made `stream` wait for the upload already)."""
+        self._refuse_deferred()
         stream = stream or torch.cuda.current_stream(self.device)
         if wait_upload and self._upload_stream is not None and self._upload_stream != stream:
             self._record_upload()
@@ -290,6 +330,7 @@ class BatchAttention:
         """Run a graph from capture() on `stream` for the last plan: waits for the plan's upload
         when it went to another stream, and counts as the run and merge of this workspace for the
         next plan's reuse checks."""
+        self._refuse_deferred()
         stream = stream or torch.cuda.current_stream(self.device)
         if self._upload_stream is not None and self._upload_stream != stream:
             self._record_upload()
@@ -303,14 +344,27 @@ class BatchAttention:
         self._consumed_stream = None
         self._run_stream = None
 
-    def merge(self, tensors: Tensors, stream=None):
+    def merge(self, tensors: Tensors, stream=None, upload_next: Optional["BatchAttention"] = None):
         """The split-KV merge of the last run (nothing when the run merged in-kernel).  On another
-        stream than the run's, the caller makes that stream wait for the run first."""
+        stream than the run's, the caller makes that stream wait for the run first.  upload_next:
+        another workspace whose last plan was made with defer_upload=True for this stream; its
+        upload goes in the same launch as the merge."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        if upload_next is not None:
+            if upload_next is self:
+                raise ValueError("upload_next must be another workspace")
+            upload_next._deferred_stream(stream)
         if self.problem.fused_merge:
             self._settle_run()
+            if upload_next is not None:
+                upload_next.upload(stream)
             return
-        stream = stream or torch.cuda.current_stream(self.device)
-        merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        if upload_next is None:
+            merge_states(self.problem, self.info, tensors, self.int_ws, self.float_ws, stream)
+        else:
+            merge_states_upload(self.problem, self.info, tensors, self.int_ws, self.float_ws, upload_next.problem,
+                                upload_next.info, upload_next.host_ws, upload_next.int_ws, stream)
+            upload_next._uploaded_on(stream)
         self._merged.record(stream)
         self._recorded(self._merged)
         self._merged_stream = stream

@@ -312,6 +312,39 @@ bsk_status check_prefill(const bsk_problem* problem, const bsk_tensors* t) {
   return BSK_OK;
 }
 
+// Copies the plan's first `used_bytes` from host_ws into the int workspace on `stream`.  Pinned
+// host memory has a device address: a kernel copies the plan from there (one launch, ordered with
+// the caller's kernels).  Other host memory goes through hipMemcpyAsync.
+bsk_status upload_plan(const void* host_ws, void* int_ws_dev, int64_t used_bytes, hipStream_t stream) {
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(host_ws), 0);
+  if (e == hipSuccess && src_dev && aligned(src_dev, 16) && aligned(int_ws_dev, 16)) {
+    e = bsk::launch_plan_upload(src_dev, int_ws_dev, used_bytes / int64_t(sizeof(int32_t)), stream);
+    if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
+  } else {
+    if (e != hipSuccess) (void)hipGetLastError();  // not pinned host memory: not an error here
+    e = hipMemcpyAsync(int_ws_dev, host_ws, size_t(used_bytes), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  }
+  return BSK_OK;
+}
+
+// The arguments of a deferred upload of a plan built by bsk_plan for `problem`.
+bsk_status check_upload(const bsk_problem* problem, const bsk_plan_info* info, const void* host_ws,
+                        size_t host_ws_bytes, const void* int_ws_dev, size_t int_ws_bytes) {
+  bsk_status s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (!info || !host_ws || !int_ws_dev) return fail(BSK_ERR_INVALID_ARG, "plan info, host and int workspaces are required");
+  s = check_plan_matches(*problem, *info);
+  if (s != BSK_OK) return s;
+  if (int_ws_bytes < bsk::plan_workspace_bytes(plan_params(*problem)))
+    return fail(BSK_ERR_WORKSPACE, "int workspace smaller than bsk_workspace_query");
+  if (info->used_bytes <= 0 || info->used_bytes % int64_t(sizeof(int32_t)) != 0 ||
+      uint64_t(info->used_bytes) > host_ws_bytes || uint64_t(info->used_bytes) > int_ws_bytes)
+    return fail(BSK_ERR_INVALID_ARG, "plan size does not fit the host or int workspace");
+  return BSK_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -416,24 +449,15 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
   info->total_cost = st.total_cost;
   info->max_load = st.max_load;
   info->used_bytes = st.used_bytes;
-  if (int_ws_dev) {
-    // Pinned host memory has a device address: a kernel on `stream` copies the plan from there
-    // (one launch, ordered with the caller's kernels).  Other host memory goes through
-    // hipMemcpyAsync.
-    void* src_dev = nullptr;
-    hipError_t e = hipHostGetDevicePointer(&src_dev, host_ws, 0);
-    if (e == hipSuccess && src_dev && aligned(src_dev, 16) && aligned(int_ws_dev, 16)) {
-      e = bsk::launch_plan_upload(src_dev, int_ws_dev, st.used_bytes / int64_t(sizeof(int32_t)),
-                                  static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return hip_fail(e, "plan upload kernel");
-    } else {
-      if (e != hipSuccess) (void)hipGetLastError();  // not pinned host memory: not an error here
-      e = hipMemcpyAsync(int_ws_dev, host_ws, size_t(st.used_bytes), hipMemcpyHostToDevice,
-                         static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
-    }
-  }
+  if (int_ws_dev) return upload_plan(host_ws, int_ws_dev, st.used_bytes, static_cast<hipStream_t>(stream));
   return BSK_OK;
+}
+
+bsk_status bsk_upload_plan(const bsk_problem* problem, const bsk_plan_info* info, const void* host_ws,
+                           size_t host_ws_bytes, void* int_ws_dev, size_t int_ws_bytes, void* stream) {
+  bsk_status s = check_upload(problem, info, host_ws, host_ws_bytes, int_ws_dev, int_ws_bytes);
+  if (s != BSK_OK) return s;
+  return upload_plan(host_ws, int_ws_dev, info->used_bytes, static_cast<hipStream_t>(stream));
 }
 
 bsk_status bsk_run_decode(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
@@ -472,6 +496,44 @@ bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* inf
   hipError_t e = bsk::launch_merge(problem->head_dim, a, merge_grid(*problem), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return BSK_OK;
+}
+
+bsk_status bsk_merge_states_upload(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                                   const void* int_ws_dev, const void* float_ws, size_t float_ws_bytes,
+                                   const bsk_problem* next_problem, const bsk_plan_info* next_info,
+                                   const void* next_host_ws, size_t next_host_ws_bytes, void* next_int_ws_dev,
+                                   size_t next_int_ws_bytes, void* stream) {
+  bsk_status s = check_upload(next_problem, next_info, next_host_ws, next_host_ws_bytes, next_int_ws_dev,
+                              next_int_ws_bytes);
+  if (s != BSK_OK) return s;
+  s = check_problem(problem);
+  if (s != BSK_OK) return s;
+  if (!info || !t || !int_ws_dev || !t->out || !t->lse) return fail(BSK_ERR_INVALID_ARG, "null argument");
+  s = check_plan_matches(*problem, *info);
+  if (s != BSK_OK) return s;
+  if (int_ws_dev == next_int_ws_dev)
+    return fail(BSK_ERR_INVALID_ARG, "the next plan must go to another int workspace than the merged run's");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*problem)))
+    return fail(BSK_ERR_WORKSPACE, "float workspace missing or smaller than bsk_workspace_query");
+  if (!aligned(t->out, problem->out_dtype == BSK_DTYPE_F32 ? 16 : 8) || t->o_stride_tok % 4 || t->o_stride_head % 4)
+    return fail(BSK_ERR_INVALID_ARG, "out must be aligned to 4 elements (strides too)");
+  const float* fw = static_cast<const float*>(float_ws);
+  const bsk::MergeArgs a =
+      merge_args(*problem, *t, int_ws_dev, fw, fw ? fw + size_t(problem->max_slots) * problem->tile_q * problem->head_dim
+                                                  : nullptr);
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(next_host_ws), 0);
+  if (e == hipSuccess && src_dev && aligned(src_dev, 16) && aligned(next_int_ws_dev, 16)) {
+    e = bsk::launch_merge_upload(problem->head_dim, a, merge_grid(*problem), src_dev, next_int_ws_dev,
+                                 next_info->used_bytes / int64_t(sizeof(int32_t)), st);
+    if (e != hipSuccess) return hip_fail(e, "merge + upload launch");
+    return BSK_OK;
+  }
+  if (e != hipSuccess) (void)hipGetLastError();  // not pinned host memory: two steps
+  e = bsk::launch_merge(problem->head_dim, a, merge_grid(*problem), st);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return upload_plan(next_host_ws, next_int_ws_dev, next_info->used_bytes, st);
 }
 
 bsk_status bsk_run_noalloc(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,

@@ -29,6 +29,9 @@ hipError_t launch_merge_pair(const float* oa, const float* la, const float* ob, 
 // Copies `words` 32-bit words from a pinned host buffer's device address into device memory, on
 // `stream`; both pointers 16-byte aligned.
 hipError_t launch_plan_upload(const void* src_dev, void* dst, int64_t words, hipStream_t stream);
+// The merge (grid `merge_grid`) and a plan upload into another workspace in one launch.
+hipError_t launch_merge_upload(int head_dim, const MergeArgs& a, int merge_grid, const void* src_dev, void* dst,
+                               int64_t words, hipStream_t stream);
 hipError_t launch_rope_table(float* table, int n_pos, int D, double theta, hipStream_t stream);
 // Device address and size of the no-allocation scratch array on the current device (looked up on
 // the first call per device).

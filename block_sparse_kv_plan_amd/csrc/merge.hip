@@ -23,7 +23,7 @@ constexpr int kMergeThreads = 256;
 // entry has more rows than min(tile_q, longest query * group): decode entries
 // (one token, a GQA group of rows) then take no idle threads.
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+__device__ __forceinline__ void merge_blocks(const MergeArgs& a, int block, int nblocks) {
   constexpr int TPR = D / 4;                  // threads per row
   constexpr int RPB = kMergeThreads / TPR;    // rows per block per pass
   const int32_t* __restrict__ ws = a.ws;
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int g = a.group;
   const int c4 = (threadIdx.x % TPR) * 4;
   const int64_t n_virtual = int64_t(n_merge) * rows;  // (entry, row) pairs
-  for (int64_t v = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR; v < n_virtual; v += int64_t(gridDim.x) * RPB) {
+  for (int64_t v = int64_t(block) * RPB + threadIdx.x / TPR; v < n_virtual; v += int64_t(nblocks) * RPB) {
     const int m = int(v / rows);
     const int rr = int(v % rows);
     const int32_t* rec = table + int64_t(m) * MERGE_WORDS;
@@ -43,6 +43,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     merge_row<D>(rec, rr, c4, tile_q, a.part_o, a.part_lse, qo_indptr[rec[MG_R]], g, a.out, a.o_st, a.o_sh, a.lse,
                  a.lse_st, a.out_bf16);
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  merge_blocks<D>(a, blockIdx.x, gridDim.x);
 }
 
 // Row-wise merge of two complete states (composable prefix + suffix).
@@ -126,14 +131,35 @@ __global__ __launch_bounds__(256) void gather_kernel(AttnArgs a, const int64_t* 
 // Plan upload: the plan's words copied from the pinned host buffer (read through its device
 // mapping) into the int workspace, by a kernel on the caller's stream.  Sixteen bytes per thread;
 // both buffers are 16-byte aligned (the host checks), the last thread takes the ragged tail.
-__global__ __launch_bounds__(256) void plan_upload_kernel(const uint32_t* __restrict__ src,
-                                                          uint32_t* __restrict__ dst, int64_t words) {
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+constexpr int kUploadWordsPerBlock = 256 * 4;
+
+__device__ __forceinline__ void upload_block(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                             int64_t words, int block) {
+  const int64_t i = (int64_t(block) * 256 + threadIdx.x) * 4;
   if (i + 4 <= words) {
     *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
   } else {
     for (int64_t k = i; k < words; ++k) dst[k] = src[k];
   }
+}
+
+__global__ __launch_bounds__(256) void plan_upload_kernel(const uint32_t* __restrict__ src,
+                                                          uint32_t* __restrict__ dst, int64_t words) {
+  upload_block(src, dst, words, blockIdx.x);
+}
+
+// One launch for the merge of one plan's run and the upload of the next plan into another
+// workspace (the two touch disjoint buffers): the first `upload_blocks` blocks copy the plan, the
+// rest merge.  The upload then needs no dispatch of its own.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_upload_kernel(MergeArgs a, int upload_blocks,
+                                                                     const uint32_t* __restrict__ src,
+                                                                     uint32_t* __restrict__ dst, int64_t words) {
+  if (int(blockIdx.x) < upload_blocks) {
+    upload_block(src, dst, words, blockIdx.x);
+    return;
+  }
+  merge_blocks<D>(a, int(blockIdx.x) - upload_blocks, int(gridDim.x) - upload_blocks);
 }
 
 // Streaming read (a measurement hook, not part of the method): every 16-byte piece of the buffer
@@ -174,7 +200,7 @@ hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int 
 }
 
 hipError_t launch_plan_upload(const void* src_dev, void* dst, int64_t words, hipStream_t stream) {
-  const int64_t grid = (words + 1023) / 1024;
+  const int64_t grid = (words + kUploadWordsPerBlock - 1) / kUploadWordsPerBlock;
   if (grid < 1 || grid > (int64_t(1) << 30)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_upload_kernel, dim3(unsigned(grid)), dim3(256), 0, stream,
                      static_cast<const uint32_t*>(src_dev), static_cast<uint32_t*>(dst), words);
@@ -186,6 +212,22 @@ hipError_t launch_merge(int head_dim, const MergeArgs& a, int grid, hipStream_t 
     hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_upload(int head_dim, const MergeArgs& a, int merge_grid, const void* src_dev, void* dst,
+                               int64_t words, hipStream_t stream) {
+  const int64_t up = (words + kUploadWordsPerBlock - 1) / kUploadWordsPerBlock;
+  if (up < 1 || merge_grid < 1 || up + merge_grid > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(up + merge_grid));
+  const uint32_t* s = static_cast<const uint32_t*>(src_dev);
+  uint32_t* d = static_cast<uint32_t*>(dst);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(merge_upload_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a, int(up), s, d, words);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(merge_upload_kernel<64>, grid, dim3(kMergeThreads), 0, stream, a, int(up), s, d, words);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -248,6 +248,21 @@ bsk_status bsk_plan(const bsk_problem* problem, int32_t batch, const int32_t* qo
                     size_t int_ws_bytes, void* stream, bsk_plan_info* info);
 
 /*
+ * The copy half of bsk_plan, for a plan built on the host only (int_ws_dev
+ * == NULL there): the first info->used_bytes of host_ws go to int_ws_dev on
+ * `stream`, by the same kernel or hipMemcpyAsync as in bsk_plan ([FI-paper,
+ * methodology 3]: the CPU plan is copied to the GPU, where a fixed launch
+ * reads it).  host_ws must stay untouched until the copy completes, and
+ * nothing may read int_ws_dev's previous plan once it is enqueued.
+ * host_ws_bytes / int_ws_bytes are the buffers' sizes; used_bytes must fit
+ * both.  Errors: INVALID_ARG (null pointers, plan / problem mismatch, a
+ * plan size that does not fit), WORKSPACE (int workspace smaller than
+ * bsk_workspace_query), HIP.
+ */
+bsk_status bsk_upload_plan(const bsk_problem* problem, const bsk_plan_info* info, const void* host_ws,
+                           size_t host_ws_bytes, void* int_ws_dev, size_t int_ws_bytes, void* stream);
+
+/*
  * Small-tile attention (16 query rows per item): decode ([FI-0.6, kernel
  * types: Decode], query length 1, GQA groups of up to 16 heads) and short
  * multi-token queries.  Persistent kernel: workgroup w runs worker w's items
@@ -296,6 +311,27 @@ bsk_status bsk_run_prefill(const bsk_problem* problem, const bsk_plan_info* info
  */
 bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
                             const void* int_ws_dev, const void* float_ws, size_t float_ws_bytes, void* stream);
+
+/*
+ * bsk_merge_states for one plan's run and bsk_upload_plan for the next plan
+ * (built on the host only, for another int workspace) in one launch on
+ * `stream`.  [FI-paper, methodology 3] copies the CPU plan to the GPU for a
+ * fixed launch; riding that copy on the previous step's merge is this
+ * library's addition: with two workspaces in turn, step k's upload then
+ * needs no dispatch of its own.  The two parts touch disjoint buffers, so
+ * int_ws_dev and next_int_ws_dev must differ.  Arguments problem ..
+ * float_ws_bytes are bsk_merge_states', next_problem .. next_int_ws_bytes
+ * bsk_upload_plan's, with the same meaning and requirements.  When
+ * next_host_ws is not pinned host memory, the merge and a hipMemcpyAsync
+ * are enqueued one after the other.  Errors: those of the two calls, and
+ * INVALID_ARG when the two int workspaces are the same; every argument is
+ * checked before anything is enqueued.
+ */
+bsk_status bsk_merge_states_upload(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,
+                                   const void* int_ws_dev, const void* float_ws, size_t float_ws_bytes,
+                                   const bsk_problem* next_problem, const bsk_plan_info* next_info,
+                                   const void* next_host_ws, size_t next_host_ws_bytes, void* next_int_ws_dev,
+                                   size_t next_int_ws_bytes, void* stream);
 
 /*
  * For callers that cannot allocate device memory or hold a float workspace:

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(bsk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -126,6 +126,41 @@ def test_merge_states_rejects_bad_workspaces_and_mismatched_plans():
     t2 = _clone(t)
     t2.out = 0x10004  # not 16-byte aligned for f32 out
     assert _merge_status(p, info, t2, fake, fake, float_b) == bsk.ERR_INVALID_ARG
+
+
+def test_upload_and_merge_upload_reject_bad_arguments():
+    """bsk_upload_plan and bsk_merge_states_upload check their arguments on the host before anything
+    is enqueued: workspaces against bsk_workspace_query, the plan against its problem and buffers,
+    and two distinct int workspaces for the merge and the upload."""
+    import ctypes as C
+    p, info, t, float_b = _planned_problem()
+    int_b, _, host_b = bsk.workspace_query(p)
+    fake, fake2, host = 0x20000, 0x40000, 0x80000
+
+    def up(i, hb, iw, ib, hw=host):
+        return bsk._lib.bsk_upload_plan(C.byref(p), C.byref(i), hw, hb, iw, ib, None)
+    assert up(info, host_b, None, int_b) == bsk.ERR_INVALID_ARG
+    assert up(info, host_b, fake, int_b, hw=None) == bsk.ERR_INVALID_ARG
+    assert up(info, host_b, fake, int_b - 4) == bsk.ERR_WORKSPACE
+    assert up(info, info.used_bytes - 4, fake, int_b) == bsk.ERR_INVALID_ARG
+    assert "does not fit" in bsk.last_error()
+    for field, value in (("tile_q", bsk.TILE_PREFILL), ("used_bytes", 0), ("used_bytes", info.used_bytes + 2)):
+        bad = _clone(info)
+        setattr(bad, field, value)
+        assert up(bad, host_b, fake, int_b) == bsk.ERR_INVALID_ARG, field
+
+    def mu(iw, fw, fb, nxt, niw, nib):
+        return bsk._lib.bsk_merge_states_upload(C.byref(p), C.byref(info), C.byref(t), iw, fw, fb, C.byref(p),
+                                                C.byref(nxt), host, host_b, niw, nib, None)
+    assert mu(fake, fake, float_b, info, fake, int_b) == bsk.ERR_INVALID_ARG
+    assert "another int workspace" in bsk.last_error()
+    assert mu(fake, None, 0, info, fake2, int_b) == bsk.ERR_WORKSPACE
+    assert mu(fake, fake, float_b - 4, info, fake2, int_b) == bsk.ERR_WORKSPACE
+    assert mu(fake, fake, float_b, info, fake2, int_b - 4) == bsk.ERR_WORKSPACE
+    assert mu(None, fake, float_b, info, fake2, int_b) == bsk.ERR_INVALID_ARG
+    bad = _clone(info)
+    bad.num_workers = info.num_workers + 1
+    assert mu(fake, fake, float_b, bad, fake2, int_b) == bsk.ERR_INVALID_ARG
 
 
 def test_run_rejects_the_same_inputs():

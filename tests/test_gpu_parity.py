@@ -399,6 +399,55 @@ def test_copy_stream_uploads_alternating_plans(fused):
         compare(bb, results[2][i][0], results[2][i][1])
 
 
+@pytest.mark.parametrize("fused", [0, 1])
+def test_deferred_uploads_ride_on_merges(fused):
+    """Two workspaces in turn, a different batch every step, each plan's upload deferred and made
+    in the same launch as the other workspace's merge of the previous step (bsk_merge_states_upload;
+    with the in-kernel merge, bsk_upload_plan beside it), behind queued work: every step's output
+    equals the same step with plain in-stream uploads, bit for bit, and the oracle."""
+    dev = require_gpu()
+    Hq, Hk, d = 32, 8, 128
+    rng = np.random.default_rng(84)
+    batches = [small(84 + i, rng.integers(1, 3000, size=int(rng.integers(3, 12))), Hq=Hq, Hk=Hk, d=d, causal=True)
+               for i in range(6)]
+    say(f"deferred uploads over 6 steps, fused merge {fused}")
+    attn = [BatchAttention.create(device=dev, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=d, dtype=bsk.DTYPE_BF16,
+                                  causal=True, max_batch=16, fused_merge=fused) for _ in range(2)]
+    dus = [upload(bb) for bb in batches]
+    main = torch.cuda.current_stream()
+    busy = torch.randn((4096, 4096), dtype=torch.float32, device=dev)
+    results = []
+    for deferred in (False, True):
+        outs = [(torch.full((int(bb.qo_indptr[-1]), Hq, d), float("nan"), dtype=torch.float32, device=dev),
+                 torch.full((int(bb.qo_indptr[-1]), Hq), float("nan"), dtype=torch.float32, device=dev))
+                for bb in batches]
+        torch.cuda.synchronize()
+        for _ in range(8):
+            busy = busy @ busy * (1.0 / 64.0)
+        prev = None
+        for i, (bb, du) in enumerate(zip(batches, dus)):
+            a = attn[i % 2]
+            t = tensors_for(a.problem, du["q"], du["k"], du["v"], outs[i][0], outs[i][1], page_indices=du["pages"])
+            if not deferred:
+                a.plan(bb.qo_indptr, bb.kv_len, du["kv_indptr"], stream=main)
+                a.run(t, stream=main)
+                continue
+            a.plan(bb.qo_indptr, bb.kv_len, du["kv_indptr"], stream=main, defer_upload=True)
+            if prev is None:
+                a.upload(main)
+            else:
+                prev[0].merge(prev[1], main, upload_next=a)
+            a.run(t, stream=main, merge=False)
+            prev = (a, t)
+        if prev is not None:
+            prev[0].merge(prev[1], main)
+        torch.cuda.synchronize()
+        results.append([(o.double().cpu().numpy(), l.double().cpu().numpy()) for o, l in outs])
+    for i, bb in enumerate(batches):
+        assert np.array_equal(results[0][i][0], results[1][i][0]) and np.array_equal(results[0][i][1], results[1][i][1])
+        compare(bb, results[1][i][0], results[1][i][1])
+
+
 # ------------------------------------------------------------------ graph capture
 
 def test_graph_capture_replan_replay():

@@ -1,7 +1,7 @@
 """The plan's upload into the int workspace: byte-identical to the host plan for a pinned host
 buffer (copied by a kernel through the buffer's device address), for a pinned buffer that starts
-inside a larger allocation, and for pageable host memory (hipMemcpyAsync); several plans in a row
-on one stream.  Checked before any attention kernel reads such a plan."""
+inside a larger allocation, for pageable host memory (hipMemcpyAsync) and for a host-only plan
+uploaded afterwards by bsk_upload_plan; several plans in a row on one stream.  Checked before any attention kernel reads such a plan."""
 import numpy as np
 import pytest
 import torch
@@ -25,7 +25,7 @@ def _lengths(b):
     return i32(b.qo_indptr), i32(b.kv_len), i32(b.kv_page_indptr)
 
 
-@pytest.mark.parametrize("kind", ["pinned", "pinned_offset", "pageable"])
+@pytest.mark.parametrize("kind", ["pinned", "pinned_offset", "pageable", "deferred"])
 def test_plan_upload_is_the_host_plan(kind):
     dev = require_gpu()
     stream = torch.cuda.current_stream()
@@ -37,13 +37,17 @@ def test_plan_upload_is_the_host_plan(kind):
         int_b, _, host_b = bsk.workspace_query(p)
         say(f"plan upload {kind}: batch {batch}")
         int_ws = torch.full((int_b,), 0xAB, dtype=torch.uint8, device=dev)
-        if kind == "pinned":
+        if kind in ("pinned", "deferred"):
             host = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
         elif kind == "pinned_offset":
             host = torch.empty(host_b + 4096, dtype=torch.uint8, pin_memory=True)[4096:]
         else:
             host = np.zeros(host_b, dtype=np.uint8)
-        info = bsk.plan(p, *_lengths(b), host, int_ws, stream)
+        if kind == "deferred":  # host-only plan, then bsk_upload_plan
+            info = bsk.plan(p, *_lengths(b), host)
+            bsk.upload_plan(p, info, host, int_ws, stream)
+        else:
+            info = bsk.plan(p, *_lengths(b), host, int_ws, stream)
         torch.cuda.synchronize()
         used = int(info.used_bytes)
         assert 0 < used <= int_b

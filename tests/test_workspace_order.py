@@ -53,15 +53,28 @@ def _attention(monkeypatch, fused, log, ws=0):
     """A BatchAttention whose launches append ("launch", kind, stream, workspace) to `log`."""
     monkeypatch.setattr(A.torch.cuda, "Event", _Ev)
     monkeypatch.setattr(A, "_HostOrderEvent", _Ev)
-    # plan(problem, qo, kv_len, kv_indptr, host_ws, int_ws, stream); run_decode and merge_states
-    # (problem, info, tensors, int_ws, float_ws, stream): int_ws carries the workspace's tag
-    monkeypatch.setattr(A, "plan", lambda *a: log.append(("launch", "upload", a[-1], a[5])))
+    # plan(problem, qo, kv_len, kv_indptr, host_ws[, int_ws, stream]) writes host_ws and, given
+    # int_ws, uploads; upload_plan(problem, info, host_ws, int_ws, stream); run_decode and
+    # merge_states (problem, info, tensors, int_ws, float_ws, stream); merge_states_upload(problem,
+    # info, tensors, int_ws, float_ws, next_problem, next_info, next_host_ws, next_int_ws, stream).
+    # host_ws and int_ws carry the workspace's tag.
+    def plan(*a):
+        log.append(("host_write", a[4]))
+        if len(a) > 5 and a[5] is not None:
+            log.append(("launch", "upload", a[6], a[5]))
+
+    def merge_states_upload(*a):
+        log.append(("launch", "merge", a[9], a[3]))
+        log.append(("launch", "upload", a[9], a[8]))
+    monkeypatch.setattr(A, "plan", plan)
+    monkeypatch.setattr(A, "upload_plan", lambda *a: log.append(("launch", "upload", a[4], a[3])))
     monkeypatch.setattr(A, "run_decode", lambda *a: log.append(("launch", "run", a[-1], a[3])))
     monkeypatch.setattr(A, "merge_states", lambda *a: log.append(("launch", "merge", a[-1], a[3])))
+    monkeypatch.setattr(A, "merge_states_upload", merge_states_upload)
     a = object.__new__(A.BatchAttention)
     a.problem = _Problem(fused)
-    a.host_ws = a.float_ws = None
-    a.int_ws = ws
+    a.float_ws = None
+    a.host_ws = a.int_ws = ws
     a.info = None
     a._init_order()
     for ev in (a._uploaded, a._consumed, a._merged):
@@ -110,17 +123,20 @@ def _done_on_host_before(log, i, at):
     return False
 
 
-def _check(log, ws=0):
+def _check(log, ws=0, min_uploads=3):
     """The hazards of workspace `ws` (launches of the other workspace only share the streams)."""
     launches = [(i, e) for i, e in enumerate(log) if e[0] == "launch" and e[3] == ws]
     uploads = [i for i, e in launches if e[1] == "upload"]
-    assert len(uploads) >= 3
+    writes = [i for i, e in enumerate(log) if e[0] == "host_write" and e[1] == ws]
+    assert len(uploads) >= min_uploads
+    # the host writes host_ws (in the plan call, after its host waits) only once every upload
+    # made from it before has completed
+    for k, h in enumerate(writes):
+        for u in uploads:
+            if u < h:
+                assert _done_on_host_before(log, u, h), f"plan {k}: previous upload not waited for"
     for k, u in enumerate(uploads):
         up_stream = log[u][2]
-        # the host writes host_ws (inside the plan call, whose host waits come before its upload
-        # launch) only after the previous upload completed
-        if k:
-            assert _done_on_host_before(log, uploads[k - 1], u), f"plan {k}: previous upload not waited for"
         for i, e in launches:
             if i >= u or e[1] == "upload":
                 continue
@@ -248,3 +264,56 @@ def test_checker_catches_lockstep(monkeypatch):
     marks = _steps(pair, log, step)
     with pytest.raises(AssertionError, match="waits for work queued after"):
         _check_pipelined(log, marks)
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_deferred_uploads_ride_on_the_other_workspace_merge(monkeypatch, fused):
+    """Two workspaces in turn, in one stream: each plan's upload is deferred and made in the same
+    launch as the other workspace's merge of the previous step (upload() for the first step, a
+    plain merge after the last).  Every hazard is excluded and the pipeline is kept."""
+    log = []
+    pair = _pair(monkeypatch, fused, log)
+    s = _stream(1, log)
+    marks, prev = [], None
+    for k in range(STEPS):
+        a = pair[k % 2]
+        marks.append(len(log))
+        a.plan(*_Z, stream=s, defer_upload=True)
+        with pytest.raises(RuntimeError, match="deferred"):
+            a.run(None, stream=s)
+        if prev is None:
+            a.upload(s)
+        else:
+            prev.merge(None, stream=s, upload_next=a)
+        a.run(None, stream=s, merge=False)
+        prev = a
+    prev.merge(None, stream=s)
+    for ws in (0, 1):
+        _check(log, ws)
+    _check_pipelined(log, marks)
+
+
+def test_deferred_upload_stream_and_target_checks(monkeypatch):
+    log = []
+    a, b = _pair(monkeypatch, 0, log)
+    s, cs = _stream(1, log), _stream(2, log)
+    with pytest.raises(RuntimeError, match="no deferred upload"):
+        a.upload(s)
+    a.plan(*_Z, stream=s, copy_stream=cs, defer_upload=True)
+    with pytest.raises(ValueError, match="stream its plan named"):
+        a.upload(s)
+    b.plan(*_Z, stream=s)
+    b.run(None, stream=s, merge=False)
+    with pytest.raises(ValueError, match="stream its plan named"):
+        b.merge(None, stream=s, upload_next=a)
+    with pytest.raises(ValueError, match="another workspace"):
+        b.merge(None, stream=s, upload_next=b)
+    a.upload(cs)
+    b.merge(None, stream=s)
+    a.run(None, stream=s)
+    # a later plan supersedes a deferred upload that was never made
+    a.plan(*_Z, stream=s, defer_upload=True)
+    a.plan(*_Z, stream=s)
+    a.run(None, stream=s)
+    for ws in (0, 1):
+        _check(log, ws, min_uploads=1)
