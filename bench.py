@@ -541,6 +541,9 @@ def main():
     ap.add_argument("--upload", choices=("copy", "stream", "merge"), default="merge",
                     help="where the Llama-3 decode leg uploads each plan: in the previous step's merge launch "
                          "(default), on the kernels' own stream, or on a copy stream the kernels wait for")
+    ap.add_argument("--rope-upload", choices=("stream", "merge"), default="merge",
+                    help="where the streaming-RoPE leg uploads each plan: in the previous step's merge launch "
+                         "(default) or on the kernels' own stream")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: first run one plain device copy of this many MiB, the reference that "
                          "scales hardware byte counters")
@@ -754,9 +757,10 @@ def main():
         # default's 528-key chunks give one wave a ninth block.  The unfused baseline uses the same plan.
         rplan = {"split_factor": 2}
         rkw = dict(rplan) if args.fused_merge is None else dict(rplan, fused_merge=args.fused_merge)
-        # a host-bound step (~38 us of GPU work): the plan goes up on the kernels' own stream
-        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, graphs=bool(args.graph), upload="stream",
-                        **rkw)
+        # a host-bound step (~38 us of GPU work): the plan goes up on the kernels' own stream, in its own
+        # launch or in the previous step's merge launch (a replayed graph holds the merge: in-stream)
+        r_up = "stream" if args.graph else args.rope_upload
+        runner = Runner(b, bsk.TILE_DECODE, copies=3, device=device, graphs=bool(args.graph), upload=r_up, **rkw)
         m = wall_clock(runner, args.steps, args.warmup, warm_s=WARM_S)
         m.update(kernel_durations(runner, max(20, min(args.steps, 100)), warm_s=WARM_S))
         secondary["streaming_rope_decode"] = {
@@ -765,7 +769,7 @@ def main():
             "kernel_gbs": round(nbytes / m["kernel_s_mean"] / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / m["kernel_s_mean"] / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_us_mean": round(m["kernel_s_mean"] * 1e6, 2), "step_us": round(m["wall_s"] * 1e6, 1),
-            "host_submit_us_median": m["host_submit_us_median"], "plan_upload": "kernels' stream",
+            "host_submit_us_median": m["host_submit_us_median"], "plan_upload": {"stream": "kernels' stream", "merge": "previous step's merge launch"}[r_up],
             "algorithmic_bytes": nbytes}
         # unfused reference point: rotate the visible keys and the query into scratch, then a plain
         # windowed decode over (rotated K, V); same bytes credited as the fused kernel's
