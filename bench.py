@@ -344,6 +344,7 @@ def ceilings(device):
     """What the vendor stack reaches on this GPU for the two bounds: a large bf16 GEMM through
     torch.matmul (hipBLASLt) and a device-to-device copy (bytes read + written).  Context for the
     roofline fractions, which are quoted against the published peaks."""
+    import numpy as np
     import torch
     stream = torch.cuda.current_stream()
     out = {}
@@ -379,11 +380,12 @@ def ceilings(device):
     out["copy_frac_of_peak"] = round(2 * src.numel() / s / 1e9 / HBM_PEAK_GBS, 4)
     del dst
     # streaming read: the library's read hook (every 16-byte piece once, non-temporal loads), best of
-    # three grid sizes
+    # four grid sizes (more workgroups than three per CU oversubscribe the memory system: a sweep read
+    # 7.0 TB/s at two or three per CU, 5.8 at four)
     import block_sparse_kv_plan_amd as bsk
     cus = torch.cuda.get_device_properties(device).multi_processor_count
     best = 0.0
-    for per_cu in (4, 8, 16):
+    for per_cu in (1, 2, 3, 4):
         grid = cus * per_cu
         sink = torch.empty(grid * 256, dtype=torch.int32, device=device)
         keep_busy(lambda i: bsk.debug_stream_read(src, sink, grid, stream), 0.05)
@@ -414,9 +416,30 @@ def ceilings(device):
     s = e0.elapsed_time(e1) * 1e-3 / (reps * 3)
     out["read_decode_volume_us"] = round(s * 1e6, 1)
     out["read_decode_volume_gbs"] = round(nb / s / 1e9, 1)
+    # the paged decode's access pattern: the 2 GiB buffer's 4 KB blocks (one kv head's 16 keys of K or V
+    # at d = 128) in a seeded random order, two blocks in flight per wave, best of four grid sizes
+    n_blk = src.numel() // 4096
+    order = torch.from_numpy(np.random.default_rng(4096).permutation(n_blk).astype(np.int32)).to(device)
+    best_b = 0.0
+    for per_cu in (1, 2, 3, 4):
+        grid = cus * per_cu
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=device)
+        keep_busy(lambda i: bsk.debug_block_read(src, order, sink, grid, stream), 0.05)
+        e0.record(stream)
+        for _ in range(reps):
+            bsk.debug_block_read(src, order, sink, grid, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3 / reps
+        if src.numel() / s / 1e9 > best_b:
+            best_b, best_bgrid = src.numel() / s / 1e9, grid
+    out["read_random_4k_blocks_gbs"] = round(best_b, 1)
+    out["read_random_4k_blocks_frac_of_peak"] = round(best_b / HBM_PEAK_GBS, 4)
+    out["read_random_4k_blocks_grid"] = best_bgrid
     out["note"] = ("GEMM: 2 n^3 flop per torch.matmul, n = 8192; copy: 2 GiB read + 2 GiB written per copy; "
-                   "read: bsk_debug_stream_read over 2 GiB, best of 4/8/16 workgroups per CU, and over the Llama-3 "
-                   "decode's 695.8 MB per launch")
+                   "read: bsk_debug_stream_read over 2 GiB, best of 1-4 workgroups per CU, and over the Llama-3 "
+                   "decode's 695.8 MB per launch; random 4 KB blocks: bsk_debug_block_read over the 2 GiB "
+                   "buffer's blocks in a seeded random order (the paged decode's access pattern)")
     del src
     return out
 

@@ -82,6 +82,7 @@ _sig = {
     "bsk_rope_table": [vp, i32, i32, f64, vp],
     "bsk_debug_gather": [P(Problem), P(PlanInfo), P(Tensors), vp, vp, vp, vp, vp],
     "bsk_debug_stream_read": [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, vp],
+    "bsk_debug_block_read": [vp, ctypes.c_size_t, vp, i32, vp, ctypes.c_size_t, i32, vp],
     "bsk_rope_apply": [P(Problem), i32, i32, vp, vp, vp, P(Tensors), vp, i64, i64, vp, vp],
     "bsk_append_paged_kv": [P(Problem), i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, i64, i64, i64,
                             i64, vp],
@@ -236,6 +237,13 @@ def debug_stream_read(src, sink, grid: int, stream=None):
     """Measurement hook: read all of src (a device buffer) once; sink receives one XOR word per
     thread."""
     _ok(_lib.bsk_debug_stream_read(_ptr(src), _nbytes(src), _ptr(sink), _nbytes(sink), int(grid), _stream(stream)))
+
+
+def debug_block_read(src, order, sink, grid: int, stream=None):
+    """Measurement hook: read the 4 KB blocks of src (a device buffer) listed in order (a device int32
+    array of block indices); sink receives one XOR word per thread."""
+    _ok(_lib.bsk_debug_block_read(_ptr(src), _nbytes(src), _ptr(order), int(order.numel()), _ptr(sink), _nbytes(sink),
+                                  int(grid), _stream(stream)))
 
 
 EXPORTED = ["bsk_status_string", "bsk_last_error", *_sig.keys()]

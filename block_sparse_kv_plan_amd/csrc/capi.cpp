@@ -715,5 +715,20 @@ bsk_status bsk_debug_stream_read(const void* src, size_t bytes, void* sink, size
   return BSK_OK;
 }
 
+bsk_status bsk_debug_block_read(const void* src, size_t bytes, const int32_t* order, int32_t n_blocks, void* sink,
+                                size_t sink_bytes, int32_t grid, void* stream) {
+  if (!src || !order || !sink) return fail(BSK_ERR_INVALID_ARG, "null argument");
+  if (!aligned(src, 16) || bytes < 4096 || bytes % 4096 != 0)
+    return fail(BSK_ERR_INVALID_ARG, "src must be 16-byte aligned, bytes a positive multiple of 4096");
+  if (!aligned(order, 4) || n_blocks <= 0) return fail(BSK_ERR_INVALID_ARG, "order must be int32-aligned, n_blocks > 0");
+  if (grid <= 0 || grid > (1 << 20)) return fail(BSK_ERR_INVALID_ARG, "grid must be in [1, 2^20]");
+  if (!aligned(sink, 4) || sink_bytes < size_t(grid) * size_t(bsk::stream_read_threads()) * sizeof(uint32_t))
+    return fail(BSK_ERR_INVALID_ARG, "sink must hold one 32-bit word per thread (grid * 256)");
+  hipError_t e = bsk::launch_block_read(src, int64_t(bytes / 4096), order, n_blocks, static_cast<uint32_t*>(sink),
+                                        grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block read launch");
+  return BSK_OK;
+}
+
 }  // extern "C"
 #pragma GCC visibility pop

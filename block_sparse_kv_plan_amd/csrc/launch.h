@@ -40,6 +40,8 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 // Reads n16 16-byte pieces of src once; sink gets one word per thread (grid * stream_read_threads()).
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int grid, hipStream_t stream);
 int stream_read_threads();
+hipError_t launch_block_read(const void* src, int64_t n_buf_blocks, const int32_t* order, int32_t n_blocks,
+                             uint32_t* sink, int grid, hipStream_t stream);
 
 hipError_t launch_gather(int dtype, int head_dim, bool dense, const AttnArgs& a, const int64_t* row_off, void* k_out,
                          void* v_out, int grid, hipStream_t stream);

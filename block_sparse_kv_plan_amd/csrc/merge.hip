@@ -191,7 +191,54 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
 
 // ---------------------------------------------------------------- host launchers
 
+// Block read (a measurement hook, not part of the method): 4 KB blocks of the buffer visited in a
+// given order, the access pattern of paged K/V (a page of one head's 16 keys is 4 KB at d = 128):
+// each wave reads whole blocks, two in flight (the decode's K and V of one key block), with 16-byte
+// non-temporal loads; block indices past the buffer are clamped to its last block.
+constexpr int kBlockWords16 = 4096 / 16;
+
+__global__ __launch_bounds__(kReadThreads) void block_read_kernel(const u32x4* __restrict__ src, int64_t n_buf_blocks,
+                                                                   const int32_t* __restrict__ order, int32_t n_blocks,
+                                                                   uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = int64_t(blockIdx.x) * (kReadThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nw = int64_t(gridDim.x) * (kReadThreads / 64);
+  auto base = [&](int64_t b) {
+    const int64_t p = min(max(int64_t(order[b]), int64_t(0)), n_buf_blocks - 1);
+    return p * kBlockWords16 + lane;
+  };
+  uint32_t x = 0;
+  int64_t b = gw;
+  for (; b + nw < n_blocks; b += 2 * nw) {
+    const int64_t p0 = base(b), p1 = base(b + nw);
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = __builtin_nontemporal_load(src + p0 + 64 * u);
+      v[4 + u] = __builtin_nontemporal_load(src + p1 + 64 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; b < n_blocks; b += nw) {
+    const int64_t p0 = base(b);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 v = __builtin_nontemporal_load(src + p0 + 64 * u);
+      x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  sink[int64_t(blockIdx.x) * kReadThreads + threadIdx.x] = x;
+}
+
 int stream_read_threads() { return kReadThreads; }
+
+hipError_t launch_block_read(const void* src, int64_t n_buf_blocks, const int32_t* order, int32_t n_blocks,
+                             uint32_t* sink, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(block_read_kernel, dim3(grid), dim3(kReadThreads), 0, stream, static_cast<const u32x4*>(src),
+                     n_buf_blocks, order, n_blocks, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kReadThreads), 0, stream, static_cast<const u32x4*>(src),

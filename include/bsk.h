@@ -459,6 +459,24 @@ bsk_status bsk_debug_gather(const bsk_problem* problem, const bsk_plan_info* inf
 bsk_status bsk_debug_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, int32_t grid,
                                  void* stream);
 
+/*
+ * Measurement hook, not part of the method: the device's practical rate for
+ * the paged decode's access pattern.  A page of one kv head's 16 keys is
+ * 4 KB of K (or V) at head_dim 128, and a page table scatters pages over the
+ * pool, so this reads n_blocks 4 KB blocks of src in the order given by
+ * `order` (a device array of n_blocks int32 block indices; an index outside
+ * [0, bytes / 4096) is clamped into it), with `grid` workgroups of 256
+ * threads, each wave reading whole blocks, two at a time, with 16-byte
+ * non-temporal loads.  sink receives one 32-bit word per thread (grid * 256
+ * words, caller-owned): the XOR of the words it read, so that for a
+ * permutation of all blocks the XOR of all of sink equals that of all of src.
+ * src: device memory, 16-byte aligned, bytes a positive multiple of 4096.
+ * Errors: INVALID_ARG (null or misaligned pointers, bad sizes, grid outside
+ * [1, 2^20], sink too small), HIP.
+ */
+bsk_status bsk_debug_block_read(const void* src, size_t bytes, const int32_t* order, int32_t n_blocks, void* sink,
+                                size_t sink_bytes, int32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

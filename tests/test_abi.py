@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(bsk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -197,3 +197,23 @@ def test_stream_read_rejects_bad_arguments():
     assert f(0x10000, 1024, 0x20000, 8 * 256 * 4 - 4, 8, None) == bsk.ERR_INVALID_ARG  # sink too small
     assert f(0x10000, 1024, 0x20000, 1 << 20, 0, None) == bsk.ERR_INVALID_ARG   # empty grid
     assert "grid" in bsk.last_error()
+
+
+def test_block_read_rejects_bad_arguments():
+    f = bsk._lib.bsk_debug_block_read
+    ok = dict(src=0x10000, nbytes=1 << 20, order=0x20000, n=16, sink=0x30000, sink_bytes=1 << 20, grid=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["src"], a["nbytes"], a["order"], a["n"], a["sink"], a["sink_bytes"], a["grid"], None)
+    assert call(src=None) == bsk.ERR_INVALID_ARG
+    assert call(order=None) == bsk.ERR_INVALID_ARG
+    assert call(sink=None) == bsk.ERR_INVALID_ARG
+    assert call(src=0x10008) == bsk.ERR_INVALID_ARG          # not 16-byte aligned
+    assert call(nbytes=4096 + 16) == bsk.ERR_INVALID_ARG     # not whole 4 KB blocks
+    assert call(nbytes=0) == bsk.ERR_INVALID_ARG
+    assert call(order=0x20002) == bsk.ERR_INVALID_ARG        # not int32-aligned
+    assert call(n=0) == bsk.ERR_INVALID_ARG
+    assert call(grid=0) == bsk.ERR_INVALID_ARG
+    assert call(grid=(1 << 20) + 1) == bsk.ERR_INVALID_ARG
+    assert call(sink_bytes=8 * 256 * 4 - 4) == bsk.ERR_INVALID_ARG
