@@ -56,3 +56,48 @@ def test_plan_upload_is_the_host_plan(kind):
         assert np.array_equal(got, want), f"first differing byte {int(np.argmax(got != want))} of {used}"
         # bytes past the plan are left alone
         assert bool((int_ws[used:used + 64] == 0xAB).all())
+
+
+@pytest.mark.parametrize("next_kind", ["pinned", "pageable"])
+def test_merge_states_upload_merges_and_uploads(next_kind):
+    """bsk_merge_states_upload: workspace A's merge and workspace B's plan upload in one call (one
+    launch for a pinned host plan, the merge then hipMemcpyAsync for pageable memory).  B's int
+    workspace receives the host plan byte for byte, and A's outputs equal those of a plain
+    bsk_merge_states of the same run, bit for bit."""
+    from block_sparse_kv_plan_amd.attention import BatchAttention, tensors_for
+    from workloads.device import upload
+    dev = require_gpu()
+    b = W.llama3_decode(batch=16)
+    du = upload(b)
+    mk = lambda: BatchAttention.create(device=dev, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
+                                       head_dim=b.head_dim, dtype=bsk.DTYPE_BF16, page_size=b.page_size,
+                                       causal=True, max_batch=64)
+    a, nxt = mk(), mk()
+    T = int(b.qo_indptr[-1])
+    outs = [(torch.full((T, b.num_qo_heads, b.head_dim), float("nan"), device=dev),
+             torch.full((T, b.num_qo_heads), float("nan"), device=dev)) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    a.plan(b.qo_indptr, b.kv_len, du["kv_indptr"], stream=stream)
+    assert a.info.num_merge > 0
+    ts = [tensors_for(a.problem, du["q"], du["k"], du["v"], o, l, page_indices=du["pages"]) for o, l in outs]
+    a.run(ts[0], stream=stream, merge=False)
+    bsk.merge_states(a.problem, a.info, ts[0], a.int_ws, a.float_ws, stream)
+    # the other batch's plan, built on the host only, for workspace B
+    b2 = W.llama3_decode(batch=64)
+    _, _, host_b = bsk.workspace_query(nxt.problem)
+    host = (torch.empty(host_b, dtype=torch.uint8, pin_memory=True) if next_kind == "pinned"
+            else np.zeros(host_b, dtype=np.uint8))
+    info2 = bsk.plan(nxt.problem, *_lengths(b2), host)
+    nxt.int_ws.fill_(0xAB)
+    say(f"merge + upload, next plan in {next_kind} memory")
+    bsk.merge_states_upload(a.problem, a.info, ts[1], a.int_ws, a.float_ws, nxt.problem, info2, host, nxt.int_ws,
+                            stream)
+    torch.cuda.synchronize()
+    used = int(info2.used_bytes)
+    want = np.asarray(host[:used]).copy() if next_kind == "pageable" else host[:used].numpy().copy()
+    assert np.array_equal(nxt.int_ws[:used].cpu().numpy(), want)
+    assert bool((nxt.int_ws[used:used + 64] == 0xAB).all())
+    # ts[1] holds only the merged rows (single-chunk rows are written by the run): compare those
+    rows = torch.isfinite(outs[1][1])
+    assert bool(rows.any())
+    assert torch.equal(outs[1][0][rows], outs[0][0][rows]) and torch.equal(outs[1][1][rows], outs[0][1][rows])
