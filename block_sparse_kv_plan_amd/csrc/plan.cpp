@@ -22,8 +22,13 @@
 //     lo = max(0, qpos(i_lo) - window + 1) if window > 0 else 0; plus the
 //     sink range [0, min(sink, lo)) when window > 0 and lo > 0.
 //  2. Total cost C = sum of (hi - lo) + |sink range| over units.
-//  3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W * split)), tile_kv)),
-//     then min(L_c, max_chunk) if max_chunk > 0.
+//  3. Chunk length L_c = max(min_chunk, roundup(ceil(C * (16 + s) / (16 W split)), tile_kv)),
+//     then min(L_c, max_chunk) if max_chunk > 0.  The slack s is 1 when
+//     tile_q = 16 (a plan of 16-row decode tiles only) and 0 otherwise:
+//     decode chunks a sixteenth longer than an even share leave fewer short
+//     remainder chunks, and for bandwidth-bound decode items one item fewer
+//     outweighs the coarser balance.  Plans with 128-row tiles keep s = 0
+//     (the mixed launch measured slower with the slack).
 //  4. A unit's chunks: with lo_a = lo rounded down to a multiple of tile_kv,
 //     [max(lo, lo_a + k L_c), min(hi, lo_a + (k+1) L_c)) for
 //     k = 0 .. (hi-1-lo_a) / L_c, then the non-empty sink range (boundaries
@@ -67,6 +72,7 @@ namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+constexpr int32_t kDecodeTileQ = 16;  // rows of a decode-class query tile (chunk slack, rule 3)
 constexpr int kWorkerBits = 20;  // the LPT assignment packs (load, worker) into 64 bits
 constexpr uint64_t kWorkerMask = (uint64_t(1) << kWorkerBits) - 1;
 inline int64_t align4(int64_t x) { return (x + 3) & ~int64_t(3); }
@@ -203,7 +209,8 @@ PlanResult build_plan(const PlanParams& p, int32_t batch, const int32_t* qo_indp
   // 2-3. total cost and chunk length
   int64_t C = 0;
   for (const Unit& u : units) C += int64_t(u.hi - u.lo) + u.sink_hi;
-  int64_t Lc = ceil_div(ceil_div(C, int64_t(W) * p.split_factor), p.tile_kv) * p.tile_kv;
+  const int64_t slack = p.tile_q == kDecodeTileQ ? 1 : 0;
+  int64_t Lc = ceil_div(ceil_div(C * (16 + slack), int64_t(W) * p.split_factor * 16), p.tile_kv) * p.tile_kv;
   Lc = std::max<int64_t>(p.min_chunk, Lc);
   if (p.max_chunk > 0) Lc = std::min<int64_t>(Lc, p.max_chunk);
   if (Lc > INT32_MAX) return fail(PLAN_INVALID, "chunk length overflows int32");

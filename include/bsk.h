@@ -225,10 +225,11 @@ bsk_status bsk_workspace_query(const bsk_problem* problem, size_t* int_ws_bytes,
  *   kv_indptr[batch+1]  PAGED: offsets into kv_page_indices;
  *                       DENSE: token offsets into k/v.
  * Each (request, kv head, query tile) is cut into key chunks of L_c =
- * max(min_chunk, roundup(ceil(total_cost / (num_workers * split_factor)),
- * tile_kv)) keys on a grid that starts at the unit's first key rounded down
- * to tile_kv (plus the sink range as its own chunk), and items are assigned
- * longest-first to the least-loaded worker.
+ * max(min_chunk, roundup(ceil(total_cost * (16 + s) / (16 * num_workers *
+ * split_factor)), tile_kv)) keys (s = 1 when tile_q = BSK_TILE_DECODE,
+ * else 0; capped by max_chunk) on a grid that starts at the unit's first
+ * key rounded down to tile_kv (plus the sink range as its own chunk), and
+ * items are assigned longest-first to the least-loaded worker.
  * Multi-chunk units write partial states to float-workspace slots; they
  * are combined in-kernel (problem.fused_merge = 1) or by bsk_merge_states.
  * The exact rules, tie-breaks included, are spelled out at the top of

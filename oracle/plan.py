@@ -24,8 +24,10 @@ independent implementation can match it bit for bit:
    gets a single unit per kv head of class 1 (the decode tile); every other
    request is tiled by tile_q as above (class 0).  Nothing else changes.
 2. Total cost C = sum over units of (hi - lo) + |sink range|.
-3. Chunk length L_c = max(min_chunk, roundup(ceil(C / (W*split_factor)), tile_kv)),
-   then min(L_c, max_chunk) when max_chunk > 0.
+3. Chunk length L_c = max(min_chunk, roundup(ceil(C*(16+s) / (16*W*split_factor)), tile_kv)),
+   then min(L_c, max_chunk) when max_chunk > 0, where the slack s is 1 for
+   a plan of 16-row (decode) query tiles only (tile_q == 16) and 0 for any
+   other tile_q: decode chunks a sixteenth longer than an even share.
 4. Chunks of a unit: with lo_a = lo rounded down to a multiple of tile_kv,
    for k = 0 .. (hi - 1 - lo_a) // L_c the range
    [max(lo, lo_a + k*L_c), min(hi, lo_a + (k+1)*L_c)) (boundaries at lo_a plus
@@ -156,7 +158,8 @@ def plan_ref(qo_len, kv_len, p: PlanParams) -> dict:
                 units.append((r, h, row_lo, row_hi, lo, hi, sink_hi))
 
     C = sum((hi - lo) + sink_hi for (_, _, _, _, lo, hi, sink_hi) in units)
-    Lc = max(p.min_chunk, _ceil_div(_ceil_div(C, W * p.split_factor), p.tile_kv) * p.tile_kv)
+    s = 1 if p.tile_q == 16 else 0
+    Lc = max(p.min_chunk, _ceil_div(_ceil_div(C * (16 + s), 16 * W * p.split_factor), p.tile_kv) * p.tile_kv)
     if p.max_chunk > 0:
         Lc = min(Lc, p.max_chunk)
 

@@ -22,7 +22,8 @@ def plan_tiny_decode():
     plan = oracle.plan_ref(b.qo_len, b.kv_len, oracle.PlanParams(**params))
     return {
         "what": "plan of the tiny fp32 paged GQA decode (kv 17/64/130/255, 8 q / 2 kv heads) on 8 workers; "
-                "C = 2*(17+64+130+255) = 932, L_c = roundup(ceil(932/16), 16) = 64, so request 2 splits "
+                "C = 2*(17+64+130+255) = 932, L_c = roundup(ceil(932*17/(16*16)), 16) = roundup(62, 16) = 64 "
+                "(decode tiles: an even share plus a sixteenth), so request 2 splits "
                 "into [0,64) [64,128) [128,130) and request 3 into four 64-token chunks",
         "source": "plan defined in oracle/plan.py (the pages give no algorithm; FlashInfer paper summary, "
                   "research methodology 3: dynamic load-balanced scheduling)",
@@ -32,7 +33,7 @@ def plan_tiny_decode():
         "chunk": int(plan["chunk"]),
         "items": plan["items"].tolist(),
         "worker_items": plan["worker_items"],
-        "merge": plan["merge"].tolist(),
+        "merge": plan["merge"][:, :6].tolist(),  # the two prefix fields are zero without a shared prefix
     }
 
 

@@ -418,6 +418,23 @@ def test_plan_window_chunks_follow_the_unit_start():
         [(4256, 4263), (0, 4)]
 
 
+def test_plan_decode_chunks_carry_a_sixteenth_of_slack():
+    """Rule 3 by hand: one request of 512 keys, 2 kv heads, 8 workers, split 1, so C = 1024 and an even
+    share is 128 keys.  A decode-tile plan (tile_q 16) targets ceil(1024 * 17 / 128) = 136 keys, rounded
+    up to 144; a 128-row plan, and a two-class plan (tile_q 128 with 16-row decode tiles), take the
+    even share of 128 itself."""
+    common = dict(num_workers=8, split_factor=1, min_chunk=16, tile_kv=16, causal=True)
+    dec = oracle.plan_ref([1], [512], _params(tile_q=16, **common))
+    assert dec["total_cost"] == 1024 and dec["chunk"] == 144
+    assert [(int(a), int(b)) for (_, h, _, _, a, b, _) in dec["items"] if h == 0] == \
+        [(0, 144), (144, 288), (288, 432), (432, 512)]
+    for kw in (dict(tile_q=128), dict(tile_q=128, decode_tile_q=16)):
+        pre = oracle.plan_ref([1], [512], _params(**kw, **common))
+        assert pre["total_cost"] == 1024 and pre["chunk"] == 128
+        assert [(int(a), int(b)) for (_, h, _, _, a, b, _) in pre["items"] if h == 0] == \
+            [(0, 128), (128, 256), (256, 384), (384, 512)]
+
+
 def test_plan_greedy_each_step_takes_least_loaded():
     kv = np.array([900, 40, 300, 1200, 7, 64])
     qo = np.ones(6, dtype=np.int64)
