@@ -511,7 +511,11 @@ bsk_status bsk_merge_states_upload(const bsk_problem* problem, const bsk_plan_in
   if (!info || !t || !int_ws_dev || !t->out || !t->lse) return fail(BSK_ERR_INVALID_ARG, "null argument");
   s = check_plan_matches(*problem, *info);
   if (s != BSK_OK) return s;
-  if (int_ws_dev == next_int_ws_dev)
+  // the merge reads its plan's first used_bytes while the upload writes the next plan's
+  if (info->used_bytes <= 0) return fail(BSK_ERR_INVALID_ARG, "plan info holds no plan");
+  const uintptr_t a0 = uintptr_t(int_ws_dev), a1 = a0 + uint64_t(info->used_bytes);
+  const uintptr_t b0 = uintptr_t(next_int_ws_dev), b1 = b0 + uint64_t(next_info->used_bytes);
+  if (a0 < b1 && b0 < a1)
     return fail(BSK_ERR_INVALID_ARG, "the next plan must go to another int workspace than the merged run's");
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (info->num_slots > 0 && (!float_ws || float_ws_bytes < float_ws_need(*problem)))

@@ -319,13 +319,15 @@ bsk_status bsk_merge_states(const bsk_problem* problem, const bsk_plan_info* inf
  * `stream`.  [FI-paper, methodology 3] copies the CPU plan to the GPU for a
  * fixed launch; riding that copy on the previous step's merge is this
  * library's addition: with two workspaces in turn, step k's upload then
- * needs no dispatch of its own.  The two parts touch disjoint buffers, so
- * int_ws_dev and next_int_ws_dev must differ.  Arguments problem ..
+ * needs no dispatch of its own.  The two parts must touch disjoint memory:
+ * the merged plan's first info->used_bytes at int_ws_dev may not overlap
+ * the next plan's first next_info->used_bytes at next_int_ws_dev.
+ * Arguments problem ..
  * float_ws_bytes are bsk_merge_states', next_problem .. next_int_ws_bytes
  * bsk_upload_plan's, with the same meaning and requirements.  When
  * next_host_ws is not pinned host memory, the merge and a hipMemcpyAsync
  * are enqueued one after the other.  Errors: those of the two calls, and
- * INVALID_ARG when the two int workspaces are the same; every argument is
+ * INVALID_ARG when those two plan ranges overlap; every argument is
  * checked before anything is enqueued.
  */
 bsk_status bsk_merge_states_upload(const bsk_problem* problem, const bsk_plan_info* info, const bsk_tensors* t,

@@ -154,6 +154,15 @@ def test_upload_and_merge_upload_reject_bad_arguments():
                                                 C.byref(nxt), host, host_b, niw, nib, None)
     assert mu(fake, fake, float_b, info, fake, int_b) == bsk.ERR_INVALID_ARG
     assert "another int workspace" in bsk.last_error()
+    # distinct pointers whose plan ranges overlap, on either side
+    assert info.used_bytes > 256
+    for niw in (fake + 256, fake - 256):
+        assert mu(fake, fake, float_b, info, niw, int_b) == bsk.ERR_INVALID_ARG
+        assert "another int workspace" in bsk.last_error()
+    bad = _clone(info)
+    bad.used_bytes = 0
+    assert bsk._lib.bsk_merge_states_upload(C.byref(p), C.byref(bad), C.byref(t), fake, fake, float_b, C.byref(p),
+                                            C.byref(info), host, host_b, fake2, int_b, None) == bsk.ERR_INVALID_ARG
     assert mu(fake, None, 0, info, fake2, int_b) == bsk.ERR_WORKSPACE
     assert mu(fake, fake, float_b - 4, info, fake2, int_b) == bsk.ERR_WORKSPACE
     assert mu(fake, fake, float_b, info, fake2, int_b - 4) == bsk.ERR_WORKSPACE
