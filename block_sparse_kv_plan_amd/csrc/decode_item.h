@@ -33,9 +33,13 @@
 // reads V straight from memory.
 //
 // Fused RoPE (bf16 cache): q and every key are rotated in fp32 with a cos/sin
-// table (the cache holds K unrotated) and rounded to fp16, whose 11-bit
-// significand keeps the logits' rounding error 8x below bf16's, so the
-// logits come from one fp16 MFMA per k-step.
+// table (the cache holds K unrotated).  Each rotated vector x is split into
+// two fp16 vectors, x1 = fp16(x) and x2 = fp16(x - x1), and a logit is
+// q1.k1 + q2.k1 + q1.k2: three fp16 MFMAs per k-step, with about 22
+// significant bits instead of fp16's 11.  A single fp16 rounding leaves each
+// logit an error of about 3e-4 (rms, d = 64 or 128), which a row whose softmax
+// one key dominates passes straight into its LSE: over 1e-3 on some rows.
+// Rotated values must stay inside fp16's range (|x| < 65504).
 
 #pragma once
 
@@ -90,6 +94,14 @@ __device__ __forceinline__ f16x8 to_f16x8(const float* f) {
     r[2 * e + 1] = h[1];
   }
   return r;
+}
+
+// What rounding to fp16 left out of 8 floats (h = to_f16x8(f)), itself rounded to fp16.
+__device__ __forceinline__ f16x8 f16_residual(const float* f, const f16x8& h) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = f[e] - float(h[e]);
+  return to_f16x8(r);
 }
 
 // Element e of four 8-element pieces (a, b, c, d), as an MFMA k-quad.
@@ -175,6 +187,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 
     bf16x8 qh[BF ? NKS : 1];
     f16x8 qr[BF && ROPE != ROPE_NONE ? NKS : 1];  // rotated q in fp16 (fused RoPE)
+    f16x8 ql[BF && ROPE != ROPE_NONE ? NKS : 1];  // ... and what that rounding left out
     float qf[BF ? 1 : NKS];
     if constexpr (BF) {
 #pragma unroll
@@ -192,10 +205,12 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
           rope8(lo, hi, reinterpret_cast<const float4*>(a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2));
           qr[s] = to_f16x8(lo);
           qr[s + HALF_KS] = to_f16x8(hi);
+          ql[s] = f16_residual(lo, qr[s]);
+          ql[s + HALF_KS] = f16_residual(hi, qr[s + HALF_KS]);
         }
         if (!row_ok) {
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) qr[s] = f16x8{};
+          for (int s = 0; s < NKS; ++s) qr[s] = ql[s] = f16x8{};
         }
       }
     } else {
@@ -342,18 +357,21 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 #pragma unroll
           for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qh[s], st, 0, 0, 0);
         } else {
-          f16x8 kr[NKS];
 #pragma unroll
           for (int s = 0; s < HALF_KS; ++s) {
             float lo[8], hi[8];
             unpack_bf16x8(kf[s], lo);
             unpack_bf16x8(kf[s + HALF_KS], hi);
             rope8(lo, hi, &cs[4 * s]);
-            kr[s] = to_f16x8(lo);
-            kr[s + HALF_KS] = to_f16x8(hi);
+            const f16x8 kl0 = to_f16x8(lo), kh0 = to_f16x8(hi);
+            const f16x8 kl1 = f16_residual(lo, kl0), kh1 = f16_residual(hi, kh0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl1, qr[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl0, ql[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl0, qr[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh1, qr[s + HALF_KS], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh0, ql[s + HALF_KS], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh0, qr[s + HALF_KS], st, 0, 0, 0);
           }
-#pragma unroll
-          for (int s = 0; s < NKS; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[s], qr[s], st, 0, 0, 0);
         }
         // st[i]: logit of key tb + 4i + j for query row n
         float sv[4], p[4];
