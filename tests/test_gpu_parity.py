@@ -91,7 +91,23 @@ def test_llama3_decode_full(split):
 def test_llama3_decode_bf16_out():
     b = W.llama3_decode(batch=16)
     O, L, _, _ = run(b, out_dtype=bsk.DTYPE_BF16)
-    compare(b, O, L)
+    compare(b, O, L, out_bf16=True)
+
+
+@pytest.mark.parametrize("tile_q,extra", [(bsk.TILE_PREFILL, {}), (bsk.TILE_PREFILL_256, {}),
+                                          (bsk.TILE_PREFILL, dict(decode_tile_q=bsk.TILE_DECODE)),
+                                          (bsk.TILE_DECODE, {})])
+def test_bf16_output_few_key_rows(tile_q, extra):
+    """bf16 output from every epilogue (prefill, mixed, decode; direct rows and the merge of split
+    units): causal rows without cache see one, two, three ... keys, so |O| is not averaged down and
+    bf16's own rounding (up to 2^-8 |O|) is part of the bound."""
+    kv = [300, 77, 2, 1, 160] if tile_q != bsk.TILE_DECODE else [300, 77, 2, 1, 1600]
+    qo = kv if tile_q != bsk.TILE_DECODE else [1, 1, 1, 1, 1]
+    b = small(74, kv, qo=qo, Hq=8, Hk=2, d=128, causal=True)
+    O, L, attn, _ = run(b, tile_q=tile_q, out_dtype=bsk.DTYPE_BF16, num_workers=8, split_factor=4, min_chunk=64,
+                        **extra)
+    assert attn.info.num_merge > 0  # some rows come out of the merge
+    compare(b, O, L, out_bf16=True)
 
 
 @pytest.mark.parametrize("case", [
