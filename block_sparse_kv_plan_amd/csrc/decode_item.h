@@ -122,6 +122,7 @@ struct DecodeSmem {
   float acc[kDecWaves * 16 * (D + 4)];
   float m[kDecWaves][16];
   float l[kDecWaves][16];
+  float lb[kDecWaves][16];
 };
 
 // SAME: K and V share page/head/token strides, so one offset serves both tensors.
@@ -140,6 +141,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
   float* s_acc = sm.acc;
   float (&s_m)[kDecWaves][16] = sm.m;
   float (&s_l)[kDecWaves][16] = sm.l;
+  float (&s_lb)[kDecWaves][16] = sm.lb;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -225,7 +227,10 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
     }
 
     const RowMask rm = row_mask(row_ok, qpos, kv_hi, a.causal, a.window, a.sink);
-    float m_run = -INFINITY, l_run = 0.f;
+    // l_run: the fp32 sum of the probabilities (the LSE); lb_run: the same probabilities as the
+    // bf16 PV operand holds them, which normalises O -- with bf16 P, dividing by l_run instead
+    // would leave a dominant key's rounding (up to 2^-9 of its V row) in O
+    float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
     f32x4 acc[NACC];
 #pragma unroll
     for (int e = 0; e < NACC; ++e) acc[e] = f32x4{0, 0, 0, 0};
@@ -252,6 +257,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
         const float m_new = grow ? bm : m_run;
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
+        lb_run *= alpha;
 #pragma unroll
         for (int e = 0; e < NACC; ++e) acc[e] *= alpha;
         m_run = m_new;
@@ -384,6 +390,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
         u32x2 pw;
         pw[0] = pack_bf16x2(p[0], p[1]);
         pw[1] = pack_bf16x2(p[2], p[3]);
+        lb_run = add_bf16x2(pw[1], add_bf16x2(pw[0], lb_run));
         const i16x4 pb = __builtin_bit_cast(i16x4, pw);
         // A operand e: element e of this lane's four V pieces = V[key 4i+j][d = 8*(n%CHUNKS) + e]
 #pragma unroll
@@ -452,9 +459,11 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
 
     // ---- combine the four waves' states through LDS (each lane owns query row n)
     l_run = wave_sum_xor16_32(l_run);
+    lb_run = BF ? wave_sum_xor16_32(lb_run) : l_run;  // fp32 P (f32 inputs) needs no second sum
     if (j == 0) {
       s_m[wave][n] = m_run;
       s_l[wave][n] = l_run;
+      s_lb[wave][n] = lb_run;
     }
     __syncthreads();
     {
@@ -489,18 +498,22 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][rr]);
-      float Lsum = 0.f;
+      float Lsum = 0.f, Lb = 0.f;
       float4 o = {0, 0, 0, 0};
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) {
-        if (s_m[w][rr] != -INFINITY) Lsum += s_l[w][rr] * __builtin_amdgcn_exp2f(s_m[w][rr] - M);
+        if (s_m[w][rr] != -INFINITY) {
+          const float sc = __builtin_amdgcn_exp2f(s_m[w][rr] - M);
+          Lsum += s_l[w][rr] * sc;
+          Lb += s_lb[w][rr] * sc;
+        }
         const float4 x = *reinterpret_cast<const float4*>(s_acc + (w * 16 + rr) * AROW + c4);
         o.x += x.x;
         o.y += x.y;
         o.z += x.z;
         o.w += x.w;
       }
-      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      const float inv = Lb > 0.f ? 1.f / Lb : 0.f;
       o.x *= inv;
       o.y *= inv;
       o.z *= inv;

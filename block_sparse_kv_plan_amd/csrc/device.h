@@ -35,6 +35,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2c_f32_bf16 against (1, 1)): the sum of
+// probabilities exactly as the PV product sees them once they are rounded to bf16.
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  const bf16x2_t one = {__bf16(1.0f), __bf16(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 // Partial states exchanged inside one launch (the in-kernel merge) pass between workgroups that
 // may run on different XCDs, whose L2 caches are not coherent with each other.  They are stored
 // and loaded as relaxed device-scope atomics (cache-coherent accesses at the device's coherence
