@@ -188,8 +188,8 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
     }
 
     bf16x8 qh[BF ? NKS : 1];
-    f16x8 qr[BF && ROPE != ROPE_NONE ? NKS : 1];  // rotated q in fp16 (fused RoPE)
-    f16x8 ql[BF && ROPE != ROPE_NONE ? NKS : 1];  // ... and what that rounding left out
+    f16x8 qr[BF && ROPE != ROPE_NONE ? NKS : 1];   // rotated q in fp16 (fused RoPE)
+    f16x8 qr2[BF && ROPE != ROPE_NONE ? NKS : 1];  // ... and what that rounding left out, in fp16
     float qf[BF ? 1 : NKS];
     if constexpr (BF) {
 #pragma unroll
@@ -207,12 +207,12 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
           rope8(lo, hi, reinterpret_cast<const float4*>(a.rope + (int64_t(pq) * (D / 2) + 8 * (4 * s + j)) * 2));
           qr[s] = to_f16x8(lo);
           qr[s + HALF_KS] = to_f16x8(hi);
-          ql[s] = f16_residual(lo, qr[s]);
-          ql[s + HALF_KS] = f16_residual(hi, qr[s + HALF_KS]);
+          qr2[s] = f16_residual(lo, qr[s]);
+          qr2[s + HALF_KS] = f16_residual(hi, qr[s + HALF_KS]);
         }
         if (!row_ok) {
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) qr[s] = ql[s] = f16x8{};
+          for (int s = 0; s < NKS; ++s) qr[s] = qr2[s] = f16x8{};
         }
       }
     } else {
@@ -369,14 +369,16 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, const int32_t* __
             unpack_bf16x8(kf[s], lo);
             unpack_bf16x8(kf[s + HALF_KS], hi);
             rope8(lo, hi, &cs[4 * s]);
-            const f16x8 kl0 = to_f16x8(lo), kh0 = to_f16x8(hi);
-            const f16x8 kl1 = f16_residual(lo, kl0), kh1 = f16_residual(hi, kh0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl1, qr[s], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl0, ql[s], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl0, qr[s], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh1, qr[s + HALF_KS], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh0, ql[s + HALF_KS], st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh0, qr[s + HALF_KS], st, 0, 0, 0);
+            // first and second fp16 part of the rotated key, for its first (lo) and second (hi) half
+            const f16x8 klo = to_f16x8(lo), khi = to_f16x8(hi);
+            const f16x8 klo2 = f16_residual(lo, klo), khi2 = f16_residual(hi, khi);
+            // the small terms first, then the main product
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(klo2, qr[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(klo, qr2[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(klo, qr[s], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(khi2, qr[s + HALF_KS], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(khi, qr2[s + HALF_KS], st, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_f16(khi, qr[s + HALF_KS], st, 0, 0, 0);
           }
         }
         // st[i]: logit of key tb + 4i + j for query row n
