@@ -359,6 +359,17 @@ def test_rope_head_dim_64():
     compare(b, O, L)
 
 
+@pytest.mark.parametrize("mode", ["absolute", "streaming"])
+def test_rope_long_items(mode):
+    """Items of the kernels' longest chunk (1024 pages = 16,384 keys): each wave then steps its
+    (cos, sin) pairs 256 times by the 64-position rotation, the longest the recurrence runs."""
+    b = small(75, [60000, 33000], Hq=8, Hk=1, d=128, causal=True, window=50000 if mode == "streaming" else 0,
+              sink=4 if mode == "streaming" else 0, rope=mode, rope_theta=500000.0, poison_invisible=True)
+    O, L, attn, _ = run(b, num_workers=4)
+    assert attn.info.chunk == 16384
+    compare(b, O, L)
+
+
 @pytest.mark.parametrize("mode,window,d", [("absolute", 1, 128), ("absolute", 1, 64), ("absolute", 2, 128),
                                            ("streaming", 3, 64)])
 def test_rope_rows_led_by_one_key(mode, window, d):
