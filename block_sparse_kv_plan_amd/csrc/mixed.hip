@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void mixed_kernel(AttnArgs a) {
       __syncthreads();  // the previous item (either class) is done with the shared LDS
       decode_item<__bf16, D, false, ROPE_NONE, SAME>(a, rec, s_mix.dec, s_pages, &s_last, kMixTileQ);
     } else if (cls == 0) {
-      prefill_item<D, false, kMixTileQ / 64, SAME>(a, rec, s_mix.pre, s_pages, &s_last);  // opens with a barrier
+      prefill_item<D, false, kMixTileQ / 64, SAME, kPreWaves, false>(a, rec, s_mix.pre, s_pages, &s_last);  // opens with a barrier
     } else {
       // the shared dense prefix of a composable batch: the batch's global query rows against the
       // prefix's own K/V, every prefix key in every query's past (no mask)
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kPreThreads, 2) void mixed_kernel(AttnArgs a) {
       ap.causal = 0;
       ap.window = 0;
       ap.sink = 0;
-      prefill_item<D, true, kMixTileQ / 64, false>(ap, rec, s_mix.pre, s_pages, &s_last);
+      prefill_item<D, true, kMixTileQ / 64, false, kPreWaves, false>(ap, rec, s_mix.pre, s_pages, &s_last);
     }
   }
 }

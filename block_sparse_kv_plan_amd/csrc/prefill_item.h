@@ -90,7 +90,9 @@ struct PrefillSmem {
 
 // SAME: K and V share page/head/token strides; a V address is the K address plus the K-to-V
 // pointer distance.
-template <int D, bool DENSE, int NB, bool SAME, int WAVES = kPreWaves>
+// SUM_MFMA: the bf16 probability sum (below) comes from one more MFMA per half against a ones
+// operand, else from v_dot2 instructions (fewer registers: the mixed launch's budget is full).
+template <int D, bool DENSE, int NB, bool SAME, int WAVES = kPreWaves, bool SUM_MFMA = true>
 __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* __restrict__ rec, PrefillSmem<D>& sm,
                                              int32_t* s_pages, int* s_last) {
   constexpr int ROWS = WAVES * 16 * NB;      // query rows per item (the plan's tile_q)
@@ -182,12 +184,20 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
     const bool wave_has_rows = wrow0 < row_hi;
     const bool all_rows = wrow0 + WROWS <= row_hi;
 
-    float m_run[NB], l_run[NB];
+    // l_run: fp32 sum of the probabilities (the LSE).  lb: the same probabilities as the bf16 PV
+    // operand holds them, which normalises O, so that a key that dominates a row contributes its V
+    // row exactly instead of with its probability's bf16 rounding (up to 2^-9 of the row).  With
+    // SUM_MFMA every element of lb_acc[nb] ends up holding the row's sum; otherwise lb_run[nb]
+    // holds this lane's share.
+    float m_run[NB], l_run[NB], lb_run[NB];
+    f32x4 lb_acc[NB];
     f32x4 acc[NB][NDB];  // acc[nb][db][i] = O^T[16 db + 4 j + i][row n of block nb]
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m_run[nb] = -INFINITY;
       l_run[nb] = 0.f;
+      lb_run[nb] = 0.f;
+      lb_acc[nb] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[nb][db] = f32x4{0, 0, 0, 0};
     }
@@ -390,6 +400,10 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
             if (bm > m_run[nb] + kPreRescaleSlack) {
               const float alpha = m_run[nb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - bm);
               l_run[nb] *= alpha;
+              if constexpr (SUM_MFMA)
+                lb_acc[nb] *= alpha;
+              else
+                lb_run[nb] *= alpha;
 #pragma unroll
               for (int db = 0; db < NDB; ++db) acc[nb][db] *= alpha;
               m_run[nb] = bm;
@@ -417,6 +431,8 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
           pb[nb] = __builtin_bit_cast(bf16x8, pw);
           // the row sum adds the fp32 values: the log-sum-exp keeps their precision
           l_run[nb] += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
+          if constexpr (!SUM_MFMA)
+            lb_run[nb] = add_bf16x2(pw[3], add_bf16x2(pw[2], add_bf16x2(pw[1], add_bf16x2(pw[0], lb_run[nb]))));
         }
       };
       // O^T[d][row] += V^T P^T for half ks.  MFMA k index 8j+e <-> key 32ks + 4j + (e&3) + 16(e>>2):
@@ -439,6 +455,12 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               acc[nb][d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pb[nb], acc[nb][d0 + i], 0, 0, 0);
+        }
+        if constexpr (SUM_MFMA) {
+          const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            lb_acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nb], lb_acc[nb], 0, 0, 0);
         }
       };
 
@@ -489,8 +511,9 @@ __device__ __forceinline__ void prefill_item(const AttnArgs& a, const int32_t* _
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float lsum = wave_sum_xor16_32(l_run[nb]);
+      const float lbsum = SUM_MFMA ? lb_acc[nb][0] : wave_sum_xor16_32(lb_run[nb]);
       if (!row_ok[nb]) continue;
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const float inv = lbsum > 0.f ? 1.f / lbsum : 0.f;
       const float lse = lsum > 0.f ? (m_run[nb] + __log2f(lsum)) * 0.69314718055994531f : -INFINITY;
       const int rr = WROWS * wave + 16 * nb + n;  // row within the tile
       const int row = row_lo + rr;

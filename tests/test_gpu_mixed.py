@@ -63,8 +63,10 @@ def test_mixed_window_sink():
 
 def test_mixed_items_match_single_class_kernels():
     """Without splits every item of the mixed launch is one the single-class kernels also run:
-    decode-class rows equal the small-tile kernel's output, the other rows the large-tile
-    kernel's, bit for bit (the same item bodies)."""
+    decode-class rows equal the small-tile kernel's output bit for bit (the same item body).  The
+    other rows have the large-tile kernel's LSE bit for bit; their O differs only in how the sum
+    of the bf16 probabilities that divides it is formed (a ones-operand MFMA in the large-tile
+    kernel, v_dot2 in the mixed launch, whose register budget is full), i.e. in the last bits."""
     qo = [1, 300, 1, 4, 1, 129, 2, 1]
     kv = [700, 1000, 33, 130, 1, 2000, 1500, 4000]
     b = small(150, kv, qo, d=128, causal=True)
@@ -78,7 +80,9 @@ def test_mixed_items_match_single_class_kernels():
     small_req = np.asarray(qo) * 4 <= bsk.TILE_DECODE
     tok_small = np.repeat(small_req, qo)
     assert np.array_equal(Om[tok_small], Od[tok_small]) and np.array_equal(Lm[tok_small], Ld[tok_small])
-    assert np.array_equal(Om[~tok_small], Op[~tok_small]) and np.array_equal(Lm[~tok_small], Lp[~tok_small])
+    assert np.array_equal(Lm[~tok_small], Lp[~tok_small])
+    # two fp32 sums of the same n bf16 values differ by at most about 2 n 2^-24 of the sum (n <= 4000)
+    np.testing.assert_allclose(Om[~tok_small], Op[~tok_small], rtol=5e-4, atol=1e-7)
     compare(b, Om, Lm)
 
 
